@@ -1,0 +1,209 @@
+"""Pins for the oracle's hybrid-tree construction (CPU only).
+
+Hand-worked examples (tests/golden), special cases that reduce to something
+computable without the construction, and invariants on random inputs.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden():
+    with open(os.path.join(GOLDEN, "build_tree_examples.json")) as f:
+        return json.load(f)
+
+
+def _one(cfg, parent, token, conf, root, prefix, m_ids):
+    n = len(parent)
+    nd = max(n, 1)
+    dp = np.full((1, nd), -1, np.int32)
+    dt = np.zeros((1, nd), np.int32)
+    dc = np.zeros((1, nd), np.float32)
+    dp[0, :n] = parent
+    dt[0, :n] = token
+    dc[0, :n] = np.asarray(conf, np.float32)
+    return O.build_tree(cfg, dp, dt, dc, np.array([n], np.int32),
+                        np.array([root], np.int32), np.array([prefix], np.int32),
+                        np.asarray(m_ids, np.int32))
+
+
+@pytest.mark.parametrize("idx", range(4))
+def test_golden_examples(idx):
+    g = _golden()
+    ex = g["examples"][idx]
+    t = _one(ex["cfg"], ex["draft_parent"], ex["draft_token"], ex["draft_conf"],
+             ex["root_token"], ex["prefix_len"], g["m_ids"])
+    e = ex["expect"]
+    assert t["token"][0].tolist() == e["token"]
+    assert t["parent"][0].tolist() == e["parent"]
+    assert t["pos"][0].tolist() == e["pos"]
+    assert t["mask"][0, :, 0].tolist() == e["mask"]
+    assert int(t["n_nodes"][0]) == e["n_nodes"]
+    assert int(t["stage"][0]) == e["stage"]
+    assert int(t["n_kept"][0]) == e["n_kept"]
+
+
+def _random_case(rng, kmax, V, S, n, max_depth, sparse_m=False):
+    cfg = dict(kmax=kmax, stage_depth=[0, 1, 5], stage_tau=[0.3, 0.3, 0.3],
+               stage_k_ret=sorted(rng.integers(0, kmax + 1, 3).tolist(), reverse=True),
+               k_ret_none=int(rng.integers(0, 3)))
+    cfg["env_parent"], cfg["env_rank"] = W.envelope(S, kmax)
+    parent = []
+    depth = []
+    for i in range(n):
+        elig = [-1] + [j for j in range(i) if depth[j] < max_depth]
+        p = elig[int(rng.integers(len(elig)))]
+        parent.append(p)
+        depth.append(1 if p < 0 else depth[p] + 1)
+    conf = rng.random(n).astype(np.float32)
+    token = rng.integers(0, V, n)
+    m_ids = np.stack([rng.permutation(V)[:S] for _ in range(V)]).astype(np.int32)
+    if sparse_m:
+        m_ids[rng.random((V, S)) < 0.3] = -1
+    root = int(rng.integers(V))
+    return cfg, parent, token, conf, root, int(rng.integers(0, 50)), m_ids
+
+
+def _walk(parent, i):
+    out = []
+    while i >= 0:
+        out.append(i)
+        i = parent[i]
+    return out
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_invariants_random(seed):
+    rng = np.random.default_rng(seed)
+    kmax = int(rng.integers(1, 40))
+    cfg, parent, token, conf, root, prefix, m_ids = _random_case(
+        rng, kmax, V=30, S=4, n=int(rng.integers(0, 50)), max_depth=8,
+        sparse_m=bool(seed % 2))
+    t = _one(cfg, parent, token, conf, root, prefix, m_ids)
+    nn = int(t["n_nodes"][0])
+    tok = t["token"][0]
+    par = t["parent"][0]
+    pos = t["pos"][0]
+    mask = t["mask"][0]
+    n_max = kmax + 1
+    assert 1 <= nn <= n_max
+    assert tok[0] == root and par[0] == -1 and pos[0] == prefix
+    for i in range(1, nn):
+        assert 0 <= par[i] < i
+    # ancestor-or-self mask agrees with a walk up the parents
+    for i in range(nn):
+        bits = {j for j in range(n_max) if (int(mask[i, j // 32]) >> (j % 32)) & 1}
+        assert bits == set(_walk(par.tolist(), i))
+        assert pos[i] == prefix + len(bits) - 1
+    # padding
+    assert (tok[nn:] == -1).all() and (par[nn:] == -1).all() and (pos[nn:] == -1).all()
+    assert (mask[nn:] == 0).all()
+    # with a full M the budget is always spent: |tree| = Kmax + root
+    if seed % 2 == 0:
+        assert nn == n_max
+    # drafts come first, then retrieval nodes; retrieval tokens are M lookups
+    nk = int(t["n_kept"][0])
+    env_parent, env_rank = cfg["env_parent"], cfg["env_rank"]
+    node_of_slot = {}
+    slot = 0
+    for i in range(1 + nk, nn):
+        # find the next valid envelope slot whose parent node matches
+        while True:
+            p = env_parent[slot]
+            ptok = root if p < 0 else (tok[node_of_slot[p]] if p in node_of_slot else None)
+            if ptok is not None and m_ids[ptok][env_rank[slot]] >= 0:
+                break
+            slot += 1
+        assert tok[i] == m_ids[ptok][env_rank[slot]]
+        assert par[i] == (0 if env_parent[slot] < 0 else node_of_slot[env_parent[slot]])
+        node_of_slot[slot] = i
+        slot += 1
+    assert slot <= kmax - nk
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_kept_set_is_best_by_path_confidence(seed):
+    """The kept drafts are the min(K_draft, #candidates) candidates that come
+    first in (path-min confidence desc, index asc) -- checked pairwise, and
+    the kept set is closed under ancestors."""
+    rng = np.random.default_rng(100 + seed)
+    kmax = int(rng.integers(1, 30))
+    cfg, parent, token, conf, root, prefix, m_ids = _random_case(
+        rng, kmax, V=20, S=3, n=int(rng.integers(1, 40)), max_depth=7)
+    token = [1000 + i for i in range(len(parent))]
+    t = _one(cfg, parent, token, conf, root, prefix, m_ids)
+    nk = int(t["n_kept"][0])
+    st = int(t["stage"][0])
+    n = len(parent)
+    ddepth = [len(_walk(parent, i)) - 1 for i in range(n)]
+    cand = [i for i in range(n) if st < 0 or ddepth[i] <= cfg["stage_depth"][st]]
+    k_draft = cfg["kmax"] - (cfg["k_ret_none"] if st < 0 else cfg["stage_k_ret"][st])
+    assert nk == max(0, min(k_draft, len(cand)))
+    pmin = [min(conf[j] for j in _walk(parent, i)) for i in range(n)]
+    # draft tokens were made distinct (1000 + index), so the output names them
+    kept = [int(x) - 1000 for x in t["token"][0][1:1 + nk]]
+    assert kept == sorted(kept) and all(0 <= a < n for a in kept)
+    assert len(kept) == nk
+    for a in kept:
+        if parent[a] >= 0:
+            assert parent[a] in kept
+        for b in cand:
+            if b not in kept:
+                assert (pmin[a], -a) > (pmin[b], -b)
+
+
+def test_stage_gate_readings():
+    """Strict comparison at tau, empty checkpoint depth never fires, first
+    firing checkpoint wins, and a firing checkpoint keeps its own level."""
+    m_ids = np.array([[1, 2]] * 10, np.int32)
+    cfg = dict(kmax=4, stage_depth=[0, 1, 5], stage_tau=[0.5, 0.5, 0.5],
+               stage_k_ret=[3, 2, 0], k_ret_none=0, env_parent=[-1, -1, 0, 0],
+               env_rank=[0, 1, 0, 1])
+    # c_0 exactly tau: not below, no fire; c_1 = 0.25 fires at stage 1
+    t = _one(cfg, [-1, 0, 1], [1, 2, 3], [0.5, 0.25, 0.9], 0, 0, m_ids)
+    assert int(t["stage"][0]) == 1
+    # stage 1 keeps depth <= 1: drafts 0 and 1, not 2
+    assert t["token"][0][1:3].tolist() == [1, 2] and int(t["n_kept"][0]) == 2
+    # depth 5 empty: nothing fires even though tau would catch anything
+    cfg2 = dict(cfg, stage_tau=[0.0, 0.0, 2.0])
+    t2 = _one(cfg2, [-1, 0, 1], [1, 2, 3], [0.5, 0.25, 0.9], 0, 0, m_ids)
+    assert int(t2["stage"][0]) == -1
+    # both d0 and d1 below tau: the first (d0) wins
+    t3 = _one(cfg, [-1, 0], [1, 2], [0.1, 0.1], 0, 0, m_ids)
+    assert int(t3["stage"][0]) == 0
+
+
+def test_no_retrieval_mode_is_topk_drafts():
+    """With k_ret_none = 0, nothing firing and at least Kmax drafts, the tree
+    is the root plus exactly Kmax drafts (the 'without retrieval' ablation)."""
+    rng = np.random.default_rng(7)
+    kmax = 10
+    cfg = dict(kmax=kmax, stage_depth=[0, 1, 5], stage_tau=[0.0, 0.0, 0.0],
+               stage_k_ret=[5, 3, 0], k_ret_none=0)
+    cfg["env_parent"], cfg["env_rank"] = W.envelope(4, kmax)
+    parent = [-1, 0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5, 6]
+    conf = rng.random(len(parent)).astype(np.float32)
+    token = list(range(100, 100 + len(parent)))
+    m_ids = np.zeros((200, 4), np.int32)
+    t = _one(cfg, parent, token, conf, 150, 0, m_ids)
+    assert int(t["n_kept"][0]) == kmax and int(t["n_nodes"][0]) == kmax + 1
+    assert all(100 <= x < 114 for x in t["token"][0][1:])
+
+
+def test_envelope_shape():
+    p, r = W.envelope(8, 60)
+    levels = []
+    d = []
+    for i, x in enumerate(p):
+        d.append(1 if x < 0 else d[x] + 1)
+    for lv in range(1, max(d) + 1):
+        levels.append(d.count(lv))
+    assert levels == [8, 16, 16, 16, 4]
+    assert r[:8] == list(range(8)) and set(r[8:24]) == {0, 1}

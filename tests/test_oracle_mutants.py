@@ -1,0 +1,96 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake into a private copy of the oracle's source (CPU
+only; the real module is untouched), points the pin tests at the copy, and
+requires at least one pin to fail.
+"""
+import importlib.util
+import inspect
+import os
+import types
+
+import pytest
+
+import oracle.graft_oracle as real
+import test_oracle_accept_update as T_au
+import test_oracle_attention as T_at
+import test_oracle_build_tree as T_bt
+
+SRC = inspect.getsource(real)
+
+MUTANTS = [
+    ("gate not strict", "if c_d < np.float32(tau):", "if c_d <= np.float32(tau):"),
+    ("firing level dropped", "if depth[i] <= stage_depth[stage]]", "if depth[i] < stage_depth[stage]]"),
+    ("cap keeps worst drafts", "key=lambda i: (-float(path_min[i]), i)", "key=lambda i: (float(path_min[i]), i)"),
+    ("cap by own conf", "path_min.append(c if parent[i] < 0 else min(c, path_min[parent[i]]))", "path_min.append(c)"),
+    ("no fill back", "k_fill = kmax - n_kept", "k_fill = min(k_ret, kmax - n_kept)"),
+    ("wrong M column", "tok = int(m_ids[parent_tok][env_rank[j]])", "tok = int(m_ids[parent_tok][0])"),
+    ("no cascade", "parent_ok, parent_tok = slot_valid[p], slot_token[p]", "parent_ok, parent_tok = True, slot_token[p]"),
+    ("slots under root", "out_parent.append(0 if env_parent[j] < 0 else slot_new[env_parent[j]])", "out_parent.append(0)"),
+    ("position off by one", "pos = [int(prefix_len) + d for d in tdepth]", "pos = [int(prefix_len) + d + 1 for d in tdepth]"),
+    ("mask without self", "anc.append({i} if p < 0 else anc[p] | {i})", "anc.append({i} if p < 0 else set(anc[p]))"),
+    ("scale dropped", "s = (K @ q[b, i, hq, :]) * scale", "s = (K @ q[b, i, hq, :])"),
+    ("wrong kv head", "by_group.setdefault((b, hq // G), [])", "by_group.setdefault((b, hq % Hkv), [])"),
+    ("V read token-major", "V = v_cache[pages, h, :, t % blk]", "V = v_cache[pages, h, t % blk, :]"),
+    ("tree keys ignore mask", "if (int(tree_mask[b, i, j // 32]) >> (j % 32)) & 1]", "]"),
+    ("partial match accepted", "full[i] = full[p] and int(tree_token[b, i]) == int(am[b, p])", "full[i] = int(tree_token[b, i]) == int(am[b, p])"),
+    ("ties to higher node", "key=lambda i: (depth[i], -i))", "key=lambda i: (depth[i], i))"),
+    ("bonus from parent", "toks = [int(tree_token[b, x]) for x in path] + [int(am[b, best])]", "toks = [int(tree_token[b, x]) for x in path] + [int(am[b, path[-2] if len(path) > 1 else best])]"),
+    ("argmax last index", "am[b, i] = int(np.argmax(row))", "am[b, i] = int(len(row) - 1 - np.argmax(row[::-1]))"),
+    ("update ties by id desc", "key=lambda kv: (-kv[1], kv[0]))[:S]", "key=lambda kv: (-kv[1], -kv[0]))[:S]"),
+    ("update forgets old score", "cand[v] = cand.get(v, 0.0) + float(c)", "cand[v] = float(c)"),
+    ("bonus transition dropped", "for k in range(L + 1):", "for k in range(L):"),
+]
+
+
+def _mutant_module(old, new):
+    assert SRC.count(old) == 1, old
+    src = SRC.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _pin_calls():
+    """Every pin test with its parameter values, as zero-arg callables."""
+    calls = []
+    for idx in range(4):
+        calls.append(lambda idx=idx: T_bt.test_golden_examples(idx))
+    for s in range(40):
+        calls.append(lambda s=s: T_bt.test_invariants_random(s))
+    for s in range(30):
+        calls.append(lambda s=s: T_bt.test_kept_set_is_best_by_path_confidence(s))
+    calls += [T_bt.test_stage_gate_readings, T_bt.test_no_retrieval_mode_is_topk_drafts]
+    for P in [0, 1, 16, 37]:
+        calls.append(lambda P=P: T_at.test_chain_equals_causal_attention(P))
+    for s in range(12):
+        calls.append(lambda s=s: T_at.test_each_row_is_dense_attention_over_its_path(s))
+    calls += [T_at.test_uniform_keys_give_mean_of_values,
+              T_at.test_single_node_is_decode_attention_and_shift_invariant,
+              T_at.test_gather_prefix_layouts]
+    for d in ["f32", "bf16"]:
+        calls.append(lambda d=d: T_au.test_accept_golden(d))
+    for s in range(25):
+        calls.append(lambda s=s: T_au.test_accept_equals_greedy_decoding_of_tiny_model(s))
+        calls.append(lambda s=s: T_au.test_accept_brute_force_over_paths(s))
+    calls += [T_au.test_accept_chain_accepts_matched_prefix,
+              T_au.test_accept_lowest_index_ties_in_bf16, T_au.test_update_golden,
+              T_au.test_prompt_seeding_is_exact_top_bigrams]
+    for s in range(20):
+        calls.append(lambda s=s: T_au.test_update_matches_brute_force_and_is_order_free(s))
+    return calls
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, monkeypatch):
+    mod = _mutant_module(old, new)
+    for t in (T_bt, T_at, T_au):
+        monkeypatch.setattr(t, "O", mod)
+    failed = 0
+    for call in _pin_calls():
+        try:
+            call()
+        except Exception:
+            failed += 1
+            break
+    assert failed, f"no pin caught the planted mistake: {name}"
