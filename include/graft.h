@@ -1,0 +1,249 @@
+/*
+ * libgraft -- the hot path of one prune-then-graft speculative-decoding step
+ * on one AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The method is the one described in "Draft Less, Retrieve More: hybrid tree
+ * construction for speculative decoding" (summary article on aitrends.kr and
+ * the paper's abstract on chatpaper.ai).  Citations below name the article's
+ * paragraphs by content: the three-point summary, the five-step method
+ * paragraph and the architecture paragraph.
+ *
+ * One decode step is four calls, enqueued on the caller's HIP stream:
+ *   graft_build_tree        prune the draft tree and refill it from M
+ *   graft_tree_attention    verify the hybrid tree with tree-masked attention
+ *   graft_accept            greedy (lossless) longest-path acceptance
+ *   graft_update_adjacency  online update of the successor table M
+ *
+ * Conventions for every call
+ *   - Every array argument is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or synchronises; scratch memory comes from a
+ *     caller workspace whose size the matching *_workspace_size query gives.
+ *   - Calls are asynchronous: they validate host-side scalars, enqueue
+ *     kernels on `stream` and return.  A non-zero status means nothing was
+ *     enqueued (GRAFT_ERR_INVALID_ARG, GRAFT_ERR_UNSUPPORTED,
+ *     GRAFT_ERR_WORKSPACE) or a launch failed (GRAFT_ERR_HIP);
+ *     graft_last_error() then returns a message (thread-local).
+ *   - Device-side contents are preconditions, not checked: parents precede
+ *     children, token ids lie in [0, vocab), counts lie within their bounds.
+ *     Out-of-range ids read by a kernel are skipped rather than dereferenced
+ *     where noted.
+ *   - Hybrid-tree arrays are [batch][n_max] with n_max = kmax + 1 (the root
+ *     is node 0 and is not counted in kmax).  Ancestor masks are
+ *     [batch][n_max][GRAFT_MASK_WORDS(n_max)] uint32, bit j of word j/32 set
+ *     when node j is the node itself or one of its ancestors.
+ *   - bf16 tensors are raw 16-bit brain-float values.
+ *   - The library is stateless and thread-safe; M is caller state.
+ */
+#ifndef GRAFT_H
+#define GRAFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t graft_status;
+enum {
+  GRAFT_OK = 0,
+  GRAFT_ERR_INVALID_ARG = -1,  /* bad scalar, null pointer or shape */
+  GRAFT_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels cover */
+  GRAFT_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  GRAFT_ERR_HIP = -4           /* a HIP call or kernel launch failed */
+};
+
+typedef enum { GRAFT_F32 = 0, GRAFT_BF16 = 1 } graft_dtype;
+
+enum {
+  GRAFT_MAX_STAGES = 8,        /* pruning checkpoints per config */
+  GRAFT_MAX_NODES = 128,       /* n_max = kmax + 1 <= 128 */
+  GRAFT_MAX_DRAFT = 256,       /* draft nodes per sequence */
+  GRAFT_MAX_TOP_S = 32         /* successors per row of M */
+};
+
+#define GRAFT_MASK_WORDS(n_max) (((n_max) + 31) / 32)
+
+/*
+ * Tree configuration (HOST memory; copied into the kernel arguments).
+ *
+ * Pruning checkpoints (method paragraph, first step; architecture paragraph:
+ * pruning at d0, d1, d5 with thresholds tau_d): at checkpoint s the largest
+ * confidence among draft nodes at draft depth stage_depth[s] (children of
+ * the root have depth 0) is compared with stage_tau[s]; the first checkpoint
+ * whose value is strictly below its threshold fires.  A checkpoint with no
+ * node at its depth does not fire.  stage_depth must be ascending.
+ *
+ * Budget split (method paragraph: Kmax = K_draft_s + K_ret_s; architecture
+ * paragraph: earlier stages give retrieval more): when stage s fires, drafts
+ * deeper than stage_depth[s] are dropped and at most kmax - stage_k_ret[s]
+ * drafts are kept (those with the highest minimum confidence along their
+ * root path, ties to the lower index).  With no firing stage the cap is
+ * kmax - k_ret_none.  The released budget is filled back to kmax proposals.
+ *
+ * Retrieval template (architecture paragraph: per-stage prefixes of a
+ * base-tree envelope filled by lookups in M; three-point summary: retrieval
+ * starts at the root): slot j of the envelope hangs below the root
+ * (env_parent[j] < 0) or below an earlier slot, and takes column
+ * env_rank[j] of M's row for its parent's token.  A stage uses the first
+ * kmax - n_kept slots.  An empty entry (-1) drops the slot and the slots
+ * below it.  env_len >= kmax.
+ */
+typedef struct {
+  int32_t kmax;                               /* 1 .. GRAFT_MAX_NODES - 1 */
+  int32_t n_stages;                           /* 0 .. GRAFT_MAX_STAGES */
+  int32_t k_ret_none;                         /* 0 .. kmax */
+  int32_t stage_depth[GRAFT_MAX_STAGES];
+  float stage_tau[GRAFT_MAX_STAGES];
+  int32_t stage_k_ret[GRAFT_MAX_STAGES];      /* 0 .. kmax */
+  int32_t env_len;                            /* kmax .. GRAFT_MAX_NODES - 1 */
+  int32_t env_parent[GRAFT_MAX_NODES - 1];
+  int32_t env_rank[GRAFT_MAX_NODES - 1];      /* 0 .. top_s - 1 */
+} graft_tree_config;
+
+/*
+ * graft_build_tree -- prune the draft tree and graft retrieved tokens.
+ * Method paragraph, first to third steps; architecture paragraph
+ * (T_s = T_draft_s U G_ret_s, |T_s| = Kmax).
+ *
+ * Inputs (device):
+ *   draft_parent, draft_token  int32 [batch][n_draft_max]; parent -1 means a
+ *                              child of the root, otherwise an earlier index
+ *   draft_conf                 float [batch][n_draft_max]
+ *   n_draft                    int32 [batch], 0 .. n_draft_max
+ *   root_token                 int32 [batch], the last verified token
+ *   prefix_len                 int32 [batch], tokens already in the KV cache
+ *   m_ids                      int32 [vocab][top_s], -1 = empty entry
+ * Outputs (device, n_max = cfg->kmax + 1):
+ *   tree_token, tree_parent, tree_pos  int32 [batch][n_max]; node 0 is the
+ *       root; then the kept drafts in input order; then the valid retrieval
+ *       slots in envelope order.  pos = prefix_len + depth (root depth 0).
+ *       Rows at or past n_nodes hold -1.
+ *   tree_mask   uint32 [batch][n_max][GRAFT_MASK_WORDS(n_max)], 0 past n_nodes
+ *   n_nodes     int32 [batch], 1 .. n_max
+ *   stage_out   int32 [batch], index of the firing checkpoint or -1
+ * One workgroup per sequence.  n_draft_max <= GRAFT_MAX_DRAFT.
+ */
+graft_status graft_build_tree(const graft_tree_config *cfg, int32_t batch,
+                              int32_t n_draft_max, const int32_t *draft_parent,
+                              const int32_t *draft_token, const float *draft_conf,
+                              const int32_t *n_draft, const int32_t *root_token,
+                              const int32_t *prefix_len, const int32_t *m_ids,
+                              int32_t vocab, int32_t top_s, int32_t *tree_token,
+                              int32_t *tree_parent, int32_t *tree_pos,
+                              uint32_t *tree_mask, int32_t *n_nodes,
+                              int32_t *stage_out, hipStream_t stream);
+
+/*
+ * graft_tree_attention -- verification attention of the hybrid tree in one
+ * pass (architecture paragraph: one target forward over the tree-attention
+ * path; abstract: draft-then-verify).
+ *
+ * For sequence b, query head hq (KV head hq / (hq_count / hkv)) and tree
+ * node i < n_nodes[b], the visible keys are all prefix tokens
+ * 0 .. prefix_len[b]-1 of b and the tree nodes j whose bit is set in
+ * tree_mask[b][i]; out = softmax(scale * q.k) weighted sum of v.  q and the
+ * keys are expected already position-rotated.  Rows i >= n_nodes[b] of out
+ * are left untouched.
+ *
+ * Layouts (device):
+ *   q, out           [batch][n_max][hq][head_dim]   (dtype)
+ *   k_tree, v_tree   [batch][n_max][hkv][head_dim]  (dtype), this step's
+ *                    tree tokens, not yet in the cache
+ *   k_cache          [num_blocks][hkv][block_size][head_dim]  token-major pages
+ *   v_cache          [num_blocks][hkv][head_dim][block_size]  dim-major pages
+ *   block_table      int32 [batch][max_blocks_per_seq]; entries past
+ *                    ceil(prefix_len/block_size) are never read
+ *   prefix_len       int32 [batch], each <= max_prefix (host bound) and
+ *                    <= max_blocks_per_seq * block_size
+ * Arithmetic: fp32 accumulation; bf16 output rounded to nearest even.
+ * Supported: block_size 16; head_dim 64 or 128 (bf16 with head_dim 128 takes
+ * the matrix-core path when n_nodes * group >= 16 rows).
+ * workspace: >= graft_tree_attention_workspace_size(...) bytes, any contents.
+ */
+size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch,
+                                           int32_t n_max, int32_t hq, int32_t hkv,
+                                           int32_t head_dim, int32_t max_prefix);
+graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                  int32_t hq, int32_t hkv, int32_t head_dim,
+                                  const void *q, const void *k_tree,
+                                  const void *v_tree, const void *k_cache,
+                                  const void *v_cache, int32_t block_size,
+                                  const int32_t *block_table,
+                                  int32_t max_blocks_per_seq,
+                                  const int32_t *prefix_len, int32_t max_prefix,
+                                  const uint32_t *tree_mask, const int32_t *n_nodes,
+                                  float scale, void *out, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * graft_accept -- lossless greedy acceptance (architecture paragraph:
+ * retrieval nodes are proposals like drafts and the output distribution is
+ * preserved; abstract: lossless), read for greedy decoding.
+ *
+ *   argmax[b][i]    lowest vocabulary index among the maxima of logits[b][i]
+ *                   (-0 equals +0); -1 for i >= n_nodes[b]
+ *   a node is accepted when every node on its root path carries the argmax
+ *   of its parent's row; the deepest accepted node wins, ties to the lower
+ *   index.
+ *   accept_len[b]   depth of the accepted node (0 = only the root)
+ *   path_nodes      int32 [batch][n_max]: root .. accepted node, -1 padded
+ *   path_tokens     int32 [batch][n_max + 1]: the path's tokens (root token
+ *                   first) followed by the accepted node's argmax (bonus),
+ *                   -1 padded; accept_len + 2 valid entries
+ * Inputs: logits [batch][n_max][vocab] (dtype); tree arrays as produced by
+ * graft_build_tree.
+ * workspace: >= graft_accept_workspace_size(...) bytes, any contents.
+ */
+size_t graft_accept_workspace_size(int32_t batch, int32_t n_max, int32_t vocab);
+graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max,
+                          int32_t vocab, const void *logits,
+                          const int32_t *tree_token, const int32_t *tree_parent,
+                          const uint32_t *tree_mask, const int32_t *n_nodes,
+                          int32_t *argmax, int32_t *accept_len,
+                          int32_t *path_nodes, int32_t *path_tokens,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * graft_update_adjacency -- online update of M (method paragraph, fourth
+ * step: M keeps learning from the verified tree; fifth step: prompt evidence
+ * for long contexts, which is this call with the prompt as one path).
+ *
+ * Path p contributes the transitions (path_tokens[p][k], path_tokens[p][k+1])
+ * for k = 0 .. accept_len[p] (the bonus token included); a negative
+ * accept_len skips the path; transitions with a token outside [0, vocab)
+ * are skipped.  Requires accept_len[p] + 2 <= path_stride.  All transitions
+ * of one call are applied together: each adds 1 to its successor's score in
+ * the predecessor's row, a successor not yet present enters with its count,
+ * and every touched row keeps its top_s best entries by (score descending,
+ * id ascending), padded with (-1, 0.0).  Scores are counts: exact while
+ * below 2^24.  Rows no transition touches are not written.
+ *
+ * m_ids int32 [vocab][top_s], m_scores float [vocab][top_s] (updated in
+ * place); path_tokens int32 [n_paths][path_stride]; accept_len int32 [n_paths].
+ * workspace: >= graft_update_adjacency_workspace_size(n_paths, path_stride)
+ * bytes.  It must be zero-filled before its first use; every call leaves it
+ * zero-filled again, so a workspace can be reused across calls without
+ * clearing.  Calls that share one workspace must not overlap.
+ */
+size_t graft_update_adjacency_workspace_size(int32_t n_paths, int32_t path_stride);
+graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t vocab,
+                                    int32_t top_s, int32_t n_paths,
+                                    int32_t path_stride, const int32_t *path_tokens,
+                                    const int32_t *accept_len, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread. */
+const char *graft_last_error(void);
+
+/* Library version string. */
+const char *graft_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRAFT_H */

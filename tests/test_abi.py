@@ -1,0 +1,117 @@
+"""The C ABI: the built library exports every call the header declares, and
+host-side validation rejects bad scalars before anything is launched.  These
+run without a GPU: every call here fails validation (or has an empty batch)
+and returns before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "graft.h")
+
+G = pytest.importorskip("tree_attention_verification_graft_amd.binding")
+lib = G.lib()
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(graft_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = header_functions()
+    for n in ["graft_build_tree", "graft_tree_attention", "graft_accept",
+              "graft_update_adjacency"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", G.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [n for n in header_functions() if n not in exported]
+    assert not missing, missing
+    assert sorted(G.EXPORTED) == header_functions()
+
+
+def _cfg(**kw):
+    c = dict(kmax=6, stage_depth=[0, 1, 5], stage_tau=[0.3] * 3, stage_k_ret=[4, 2, 0],
+             k_ret_none=0, env_parent=[-1, -1, 0, 0, 1, 1], env_rank=[0, 1, 0, 1, 0, 1])
+    c.update(kw)
+    return G.make_config(c)
+
+
+def _build(cfg, batch=1, n_draft_max=8, vocab=10, top_s=2):
+    return lib.graft_build_tree(ctypes.byref(cfg), batch, n_draft_max, *([FAKE] * 7), vocab,
+                                top_s, *([FAKE] * 6), None)
+
+
+def test_build_tree_validation():
+    assert _build(_cfg(kmax=0)) == -1
+    assert _build(_cfg(kmax=200)) == -1
+    assert _build(_cfg(stage_k_ret=[7, 2, 0])) == -1          # K_ret > kmax
+    assert _build(_cfg(stage_depth=[1, 0, 5])) == -1          # not ascending
+    assert _build(_cfg(env_parent=[-1, -1, 0, 3, 1, 1])) == -1  # parent after slot
+    assert _build(_cfg(env_rank=[0, 1, 0, 2, 0, 1])) == -1    # rank >= top_s
+    assert _build(_cfg(env_parent=[-1, -1, 0], env_rank=[0, 1, 0])) == -1  # env < kmax
+    assert _build(_cfg(), n_draft_max=300) == -2
+    assert _build(_cfg(), top_s=0) == -1
+    assert "top_s" in G.graft_last_error()
+    assert _build(_cfg(), batch=0) == 0                       # nothing to do
+
+
+def _attn(dtype=1, batch=1, n_max=17, hq=4, hkv=1, D=128, block=16, max_blocks=8,
+          max_prefix=128, ws=None, ws_bytes=0, scale=0.1):
+    return lib.graft_tree_attention(dtype, batch, n_max, hq, hkv, D, *([FAKE] * 5), block,
+                                    FAKE, max_blocks, FAKE, max_prefix, FAKE, FAKE,
+                                    ctypes.c_float(scale), FAKE, ws, ws_bytes, None)
+
+
+def test_attention_validation():
+    assert _attn(dtype=7) == -1
+    assert _attn(D=96) == -2
+    assert _attn(block=32) == -2
+    assert _attn(hq=6, hkv=4) == -1
+    assert _attn(n_max=129) == -1
+    assert _attn(max_blocks=2) == -1                          # 2*16 < max_prefix
+    assert _attn(scale=float("inf")) == -1
+    assert _attn(batch=0) == 0
+    # a long prefix needs split partials: no workspace -> workspace error
+    need = lib.graft_tree_attention_workspace_size(1, 1, 61, 32, 8, 128, 65536)
+    assert need > 0
+    assert _attn(n_max=61, hq=32, hkv=8, max_blocks=4096, max_prefix=65536) == -3
+    assert "workspace" in G.graft_last_error()
+
+
+def test_accept_and_update_validation():
+    acc = lambda **k: lib.graft_accept(k.get("dt", 1), k.get("b", 1), k.get("n", 17),
+                                       k.get("v", 1000), *([FAKE] * 9), k.get("ws", FAKE),
+                                       k.get("wsb", 1 << 20), None)
+    assert acc(dt=3) == -1
+    assert acc(n=200) == -1
+    assert acc(v=0) == -1
+    assert acc(wsb=8) == -3
+    assert acc(b=0) == 0
+    assert lib.graft_accept_workspace_size(2, 65, 151936) == 2 * 65 * 10 * 8 // 256 * 256 + (
+        256 if (2 * 65 * 10 * 8) % 256 else 0)
+    upd = lambda **k: lib.graft_update_adjacency(FAKE, FAKE, k.get("v", 100), k.get("s", 8),
+                                                 k.get("np", 4), k.get("st", 10), FAKE, FAKE,
+                                                 k.get("ws", FAKE), k.get("wsb", 1 << 20),
+                                                 None)
+    assert upd(s=0) == -1
+    assert upd(s=33) == -1
+    assert upd(v=0) == -1
+    assert upd(wsb=100) == -3
+    assert upd(np=0) == 0                                     # no transitions
+    small = lib.graft_update_adjacency_workspace_size(4, 10)
+    big = lib.graft_update_adjacency_workspace_size(1, 65536)
+    assert 0 < small < big
+
+
+def test_version_string():
+    assert "gfx950" in G.graft_version()

@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path against the oracle on the same seeded inputs.
+
+Bit-exact: hybrid trees (tokens, parents, positions, masks, node counts,
+firing stage), argmax, accepted paths, and the adjacency table after the
+update.  Attention: max-abs error against the float64 oracle within 1e-2 for
+bf16 inputs (fp32 accumulation, bf16 output) and 1e-4 for fp32.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _f64(a, dtype):
+    return O.as_f64(a, dtype)
+
+
+def oracle_tree(w, m_ids=None):
+    return O.build_tree(w.cfg, w.draft_parent, w.draft_token, w.draft_conf, w.n_draft,
+                        w.root_token, w.prefix_len, w.m_ids if m_ids is None else m_ids)
+
+
+def check_tree(gpu, ref):
+    nn = ref["n_nodes"]
+    np.testing.assert_array_equal(gpu["n_nodes"], nn)
+    np.testing.assert_array_equal(gpu["stage"], ref["stage"])
+    np.testing.assert_array_equal(gpu["token"], ref["token"])
+    np.testing.assert_array_equal(gpu["parent"], ref["parent"])
+    np.testing.assert_array_equal(gpu["pos"], ref["pos"])
+    np.testing.assert_array_equal(gpu["mask"], ref["mask"])
+
+
+def check_attention(w, out_gpu, tree, rows=None):
+    from tree_attention_verification_graft_amd.pipeline import to_host
+    got = _f64(to_host(out_gpu), w.dtype)
+    ref = O.tree_attention(_f64(w.q, w.dtype), _f64(w.k_tree, w.dtype), _f64(w.v_tree, w.dtype),
+                           _f64(w.k_cache, w.dtype), _f64(w.v_cache, w.dtype), w.block_table,
+                           w.prefix_len, tree["mask"], tree["n_nodes"], w.scale, rows=rows)
+    if rows is None:
+        rows = [(b, i, h) for b in range(w.B) for i in range(int(tree["n_nodes"][b]))
+                for h in range(w.Hq)]
+    err = max(float(np.abs(got[b, i, h] - ref[b, i, h]).max()) for (b, i, h) in rows)
+    assert np.isfinite(err) and err <= TOL[w.dtype], f"attention max-abs {err}"
+    return err
+
+
+def run_full_check(w, attn_rows=None, seed_prompt=False):
+    """Whole step on the GPU vs the oracle: build, attention, accept (with a
+    planted path), update."""
+    import torch
+    from tree_attention_verification_graft_amd.pipeline import DeviceStep, to_host
+    _say(f"[parity] {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+         f"P={w.prefix_len.tolist()[:8]} kmax={w.kmax} V={w.V}")
+    m_ids, m_scores = w.m_ids, w.m_scores
+    if seed_prompt:
+        m_ids, m_scores = O.update_adjacency(m_ids, m_scores, w.prompt[None],
+                                             np.array([len(w.prompt) - 2]))
+    ref_tree = oracle_tree(w, m_ids)
+    logits = W.plant_path(w.logits, w.dtype, ref_tree["token"], ref_tree["parent"],
+                          ref_tree["n_nodes"], w.plant_seed)
+    ds = DeviceStep(w, logits=logits, alloc_update_for_prompt=seed_prompt)
+    if seed_prompt:
+        ds.seed_from_prompt(w.prompt)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(ds.m_ids), m_ids)
+        np.testing.assert_array_equal(to_host(ds.m_scores), m_scores)
+    ds.build()
+    torch.cuda.synchronize()
+    check_tree(ds.tree_host(), ref_tree)
+    ds.attention()
+    torch.cuda.synchronize()
+    err = check_attention(w, ds.out, ref_tree, rows=attn_rows)
+    ds.accept()
+    torch.cuda.synchronize()
+    ref_acc = O.accept(logits, w.dtype, ref_tree["token"], ref_tree["parent"],
+                       ref_tree["n_nodes"])
+    np.testing.assert_array_equal(to_host(ds.argmax), ref_acc["argmax"])
+    np.testing.assert_array_equal(to_host(ds.accept_len), ref_acc["accept_len"])
+    np.testing.assert_array_equal(to_host(ds.path_nodes), ref_acc["path_nodes"])
+    np.testing.assert_array_equal(to_host(ds.path_tokens), ref_acc["path_tokens"])
+    ds.update()
+    torch.cuda.synchronize()
+    ref_ids, ref_sc = O.update_adjacency(m_ids, m_scores, ref_acc["path_tokens"],
+                                         ref_acc["accept_len"])
+    np.testing.assert_array_equal(to_host(ds.m_ids), ref_ids)
+    np.testing.assert_array_equal(to_host(ds.m_scores), ref_sc)
+    _say(f"[parity] {w.name}: ok, attention max-abs {err:.2e}, "
+         f"accept_len {ref_acc['accept_len'].tolist()[:8]}")
+    return ds
+
+
+# ----------------------------------------------------------------------------
+# oracle-sized variants of the five workloads (several tiles, ragged tails)
+# ----------------------------------------------------------------------------
+
+SMALL = {
+    "tiny_f32": dict(),
+    "llama3_8b_b1": dict(B=2, Hq=8, Hkv=2, prefix_list=[300, 777], V=4096),
+    "qwen3_8b_b16": dict(B=6, Hq=8, Hkv=2, prefix=(40, 700), V=8192),
+    "llama31_8b_64k": dict(Hq=8, Hkv=2, prefix=(3000, 3000), V=5000),
+    "qwen3_235b_share": dict(B=3, Hq=32, Hkv=2, prefix=(500, 500), V=6000),
+}
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_small_variant(name):
+    w = W.make(name, **SMALL[name])
+    run_full_check(w, seed_prompt=w.prompt is not None)
+
+
+EDGE = [
+    # empty prefixes, a one-token prefix, exact page/tile boundaries
+    ("prefix_edges", "qwen3_8b_b16", dict(B=5, Hq=8, Hkv=2, prefix_list=[0, 1, 16, 64, 65],
+                                          V=2048)),
+    # no drafts at all (pure retrieval) and single-draft sequences
+    ("no_drafts", "llama3_8b_b1", dict(B=3, Hq=8, Hkv=2, prefix_list=[100, 200, 5],
+                                       n_draft_list=[0, 1, 60], V=1024)),
+    # fewer than 16 query rows: bf16 takes the wavefront path
+    ("few_rows_bf16", "llama3_8b_b1", dict(B=2, Hq=8, Hkv=2, kmax=2, stage_k_ret=[1, 1, 0],
+                                          n_draft=4, prefix_list=[129, 300], V=512)),
+    # the largest tree: kmax 127 (4 mask words), 256 drafts, 4-row groups
+    ("max_tree", "qwen3_8b_b16", dict(B=2, Hq=8, Hkv=4, kmax=127, stage_k_ret=[64, 32, 0],
+                                      n_draft=256, prefix_list=[90, 1000], V=3000)),
+    # vocab not a multiple of 8 (scalar argmax loads), fp32 head dim 128
+    ("odd_vocab_f32", "tiny_f32", dict(D=128, V=999, prefix=(77, 77))),
+    # GQA group 16 with several row groups and a split prefix
+    ("group16_long", "qwen3_235b_share", dict(B=2, Hq=32, Hkv=2, prefix_list=[2500, 4100],
+                                              V=3000)),
+]
+
+
+@pytest.mark.parametrize("label,name,over", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_case(label, name, over):
+    w = W.make(name, **over)
+    run_full_check(w)
+
+
+def test_update_is_deterministic_and_workspace_stays_clean():
+    """Two identical updates from the same state give bit-identical tables,
+    and the workspace is all-zero after each call."""
+    import torch
+    from tree_attention_verification_graft_amd import binding as G
+    from tree_attention_verification_graft_amd.pipeline import to_device, to_host
+    rng = np.random.default_rng(3)
+    V, S = 500, 8
+    ids, sc = W.synth.seeded_adjacency(rng, V, S, W.Zipf(V))
+    paths = W.Zipf(V).draw(rng, (40, 66)).astype(np.int32)
+    acc = rng.integers(-1, 64, 40).astype(np.int32)
+    ws = torch.zeros(G.graft_update_adjacency_workspace_size(40, 66), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for _ in range(2):
+        d_ids, d_sc = to_device(ids, "cuda"), to_device(sc, "cuda")
+        G.graft_update_adjacency(d_ids, d_sc, to_device(paths, "cuda"), to_device(acc, "cuda"),
+                                 ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+        outs.append((to_host(d_ids), to_host(d_sc)))
+    ref = O.update_adjacency(ids, sc, paths, acc)
+    for o in outs:
+        np.testing.assert_array_equal(o[0], ref[0])
+        np.testing.assert_array_equal(o[1], ref[1])
+
+
+def test_attention_is_deterministic():
+    import torch
+    from tree_attention_verification_graft_amd.pipeline import DeviceStep
+    w = W.make("qwen3_8b_b16", B=4, Hq=8, Hkv=2, prefix=(300, 3000), V=1024)
+    ds = DeviceStep(w)
+    ds.build()
+    ds.attention()
+    a = ds.out.clone()
+    ds.attention()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), ds.out.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times;
+# attention checked on sampled rows
+# ----------------------------------------------------------------------------
+
+def _sample_rows(w, tree, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(w.B):  # the last node of every sequence (deepest tree keys)
+        rows.add((b, int(tree["n_nodes"][b]) - 1, int(rng.integers(w.Hq))))
+    while len(rows) < n:
+        b = int(rng.integers(w.B))
+        rows.add((b, int(rng.integers(int(tree["n_nodes"][b]))), int(rng.integers(w.Hq))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_full_size(name):
+    w = W.make(name)
+    seed = w.prompt is not None
+    m_ids = w.m_ids
+    if seed:
+        m_ids = O.update_adjacency(w.m_ids, w.m_scores, w.prompt[None],
+                                   np.array([len(w.prompt) - 2]))[0]
+    rows = _sample_rows(w, oracle_tree(w, m_ids), 48, 7)
+    run_full_check(w, attn_rows=rows, seed_prompt=seed)

@@ -1,0 +1,326 @@
+// Host side of the C ABI: argument validation, launch planning, workspace
+// carving.  No allocation, no synchronisation: every call only enqueues
+// kernels on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "graft_internal.h"
+
+namespace graft {
+
+static thread_local char g_error[512] = "";
+
+graft_status set_error(graft_status code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+graft_status check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_error(GRAFT_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return GRAFT_OK;
+}
+
+}  // namespace graft
+
+using namespace graft;
+
+#define REQUIRE(cond, code, ...)               \
+  do {                                         \
+    if (!(cond)) return set_error(code, __VA_ARGS__); \
+  } while (0)
+
+extern "C" {
+
+const char *graft_last_error(void) { return g_error; }
+
+const char *graft_version(void) { return "libgraft 0.1 (gfx950)"; }
+
+// --------------------------------------------------------------- build tree
+graft_status graft_build_tree(const graft_tree_config *cfg, int32_t batch,
+                              int32_t n_draft_max, const int32_t *draft_parent,
+                              const int32_t *draft_token, const float *draft_conf,
+                              const int32_t *n_draft, const int32_t *root_token,
+                              const int32_t *prefix_len, const int32_t *m_ids,
+                              int32_t vocab, int32_t top_s, int32_t *tree_token,
+                              int32_t *tree_parent, int32_t *tree_pos,
+                              uint32_t *tree_mask, int32_t *n_nodes,
+                              int32_t *stage_out, hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(cfg, GRAFT_ERR_INVALID_ARG, "graft_build_tree: cfg is null");
+  REQUIRE(batch >= 0, GRAFT_ERR_INVALID_ARG, "graft_build_tree: batch < 0");
+  REQUIRE(cfg->kmax >= 1 && cfg->kmax <= GRAFT_MAX_NODES - 1, GRAFT_ERR_INVALID_ARG,
+          "graft_build_tree: kmax %d outside 1..%d", cfg->kmax, GRAFT_MAX_NODES - 1);
+  REQUIRE(cfg->n_stages >= 0 && cfg->n_stages <= GRAFT_MAX_STAGES, GRAFT_ERR_INVALID_ARG,
+          "graft_build_tree: n_stages %d outside 0..%d", cfg->n_stages, GRAFT_MAX_STAGES);
+  REQUIRE(cfg->k_ret_none >= 0 && cfg->k_ret_none <= cfg->kmax, GRAFT_ERR_INVALID_ARG,
+          "graft_build_tree: k_ret_none outside 0..kmax");
+  for (int s = 0; s < cfg->n_stages; ++s) {
+    REQUIRE(cfg->stage_k_ret[s] >= 0 && cfg->stage_k_ret[s] <= cfg->kmax, GRAFT_ERR_INVALID_ARG,
+            "graft_build_tree: stage_k_ret[%d] outside 0..kmax", s);
+    REQUIRE(cfg->stage_depth[s] >= 0, GRAFT_ERR_INVALID_ARG,
+            "graft_build_tree: stage_depth[%d] < 0", s);
+    REQUIRE(s == 0 || cfg->stage_depth[s] > cfg->stage_depth[s - 1], GRAFT_ERR_INVALID_ARG,
+            "graft_build_tree: stage_depth must be ascending");
+    REQUIRE(!std::isnan(cfg->stage_tau[s]), GRAFT_ERR_INVALID_ARG,
+            "graft_build_tree: stage_tau[%d] is NaN", s);
+  }
+  REQUIRE(cfg->env_len >= cfg->kmax && cfg->env_len <= GRAFT_MAX_NODES - 1,
+          GRAFT_ERR_INVALID_ARG, "graft_build_tree: env_len must be in kmax..%d",
+          GRAFT_MAX_NODES - 1);
+  REQUIRE(top_s >= 1 && top_s <= GRAFT_MAX_TOP_S, GRAFT_ERR_INVALID_ARG,
+          "graft_build_tree: top_s outside 1..%d", GRAFT_MAX_TOP_S);
+  REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_build_tree: vocab < 1");
+  for (int j = 0; j < cfg->env_len; ++j) {
+    REQUIRE(cfg->env_parent[j] < j, GRAFT_ERR_INVALID_ARG,
+            "graft_build_tree: env_parent[%d] must precede its slot", j);
+    REQUIRE(cfg->env_rank[j] >= 0 && cfg->env_rank[j] < top_s, GRAFT_ERR_INVALID_ARG,
+            "graft_build_tree: env_rank[%d] outside 0..top_s-1", j);
+  }
+  REQUIRE(n_draft_max >= 0 && n_draft_max <= GRAFT_MAX_DRAFT, GRAFT_ERR_UNSUPPORTED,
+          "graft_build_tree: n_draft_max %d outside 0..%d", n_draft_max, GRAFT_MAX_DRAFT);
+  if (batch == 0) return GRAFT_OK;
+  REQUIRE((n_draft_max == 0 || (draft_parent && draft_token && draft_conf)) && n_draft &&
+              root_token && prefix_len && m_ids && tree_token && tree_parent && tree_pos &&
+              tree_mask && n_nodes && stage_out,
+          GRAFT_ERR_INVALID_ARG, "graft_build_tree: null device pointer");
+
+  BuildParams p{};
+  p.cfg = *cfg;
+  for (int j = cfg->env_len; j < GRAFT_MAX_NODES - 1; ++j) {
+    p.cfg.env_parent[j] = -1;
+    p.cfg.env_rank[j] = 0;
+  }
+  p.batch = batch;
+  p.n_draft_max = n_draft_max;
+  p.vocab = vocab;
+  p.top_s = top_s;
+  p.n_max = cfg->kmax + 1;
+  p.words = GRAFT_MASK_WORDS(p.n_max);
+  p.draft_parent = draft_parent;
+  p.draft_token = draft_token;
+  p.draft_conf = draft_conf;
+  p.n_draft = n_draft;
+  p.root_token = root_token;
+  p.prefix_len = prefix_len;
+  p.m_ids = m_ids;
+  p.tree_token = tree_token;
+  p.tree_parent = tree_parent;
+  p.tree_pos = tree_pos;
+  p.tree_mask = tree_mask;
+  p.n_nodes = n_nodes;
+  p.stage_out = stage_out;
+  launch_build_tree(p, stream);
+  return check_launch("graft_build_tree");
+}
+
+// ---------------------------------------------------------------- attention
+static graft_status check_attn_shape(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                     int32_t hq, int32_t hkv, int32_t head_dim,
+                                     int32_t max_prefix) {
+  REQUIRE(dtype == GRAFT_F32 || dtype == GRAFT_BF16, GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention: unknown dtype %d", (int)dtype);
+  REQUIRE(batch >= 0 && n_max >= 1 && n_max <= GRAFT_MAX_NODES, GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention: batch/n_max out of range");
+  REQUIRE(hq >= 1 && hkv >= 1 && hq % hkv == 0, GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention: hq must be a positive multiple of hkv");
+  REQUIRE(head_dim == 64 || head_dim == 128, GRAFT_ERR_UNSUPPORTED,
+          "graft_tree_attention: head_dim %d not supported (64 or 128)", head_dim);
+  REQUIRE(max_prefix >= 0, GRAFT_ERR_INVALID_ARG, "graft_tree_attention: max_prefix < 0");
+  REQUIRE((long long)batch * hkv * (hq / hkv) < (1LL << 24), GRAFT_ERR_UNSUPPORTED,
+          "graft_tree_attention: too many heads x sequences");
+  return GRAFT_OK;
+}
+
+size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                           int32_t hq, int32_t hkv, int32_t head_dim,
+                                           int32_t max_prefix) {
+  if (check_attn_shape(dtype, batch, n_max, hq, hkv, head_dim, max_prefix) != GRAFT_OK)
+    return 0;
+  const AttnPlan pl = plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
+  return align_up(pl.part_o_bytes, 256) + align_up(pl.part_ml_bytes, 256);
+}
+
+graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                  int32_t hq, int32_t hkv, int32_t head_dim,
+                                  const void *q, const void *k_tree, const void *v_tree,
+                                  const void *k_cache, const void *v_cache,
+                                  int32_t block_size, const int32_t *block_table,
+                                  int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                                  int32_t max_prefix, const uint32_t *tree_mask,
+                                  const int32_t *n_nodes, float scale, void *out,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  g_error[0] = 0;
+  graft_status st = check_attn_shape(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
+  if (st != GRAFT_OK) return st;
+  REQUIRE(block_size == 16, GRAFT_ERR_UNSUPPORTED,
+          "graft_tree_attention: block_size %d not supported (16)", block_size);
+  REQUIRE(max_blocks_per_seq >= 1 &&
+              (long long)max_blocks_per_seq * block_size >= (long long)max_prefix,
+          GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention: max_blocks_per_seq * block_size < max_prefix");
+  REQUIRE(std::isfinite(scale), GRAFT_ERR_INVALID_ARG, "graft_tree_attention: scale not finite");
+  if (batch == 0) return GRAFT_OK;
+  REQUIRE(q && k_tree && v_tree && k_cache && v_cache && block_table && prefix_len &&
+              tree_mask && n_nodes && out,
+          GRAFT_ERR_INVALID_ARG, "graft_tree_attention: null device pointer");
+
+  const AttnPlan pl = plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
+  const size_t need = align_up(pl.part_o_bytes, 256) + align_up(pl.part_ml_bytes, 256);
+  REQUIRE(need == 0 || (workspace && workspace_bytes >= need), GRAFT_ERR_WORKSPACE,
+          "graft_tree_attention: workspace of %zu bytes needed, %zu given", need,
+          workspace_bytes);
+
+  AttnParams p{};
+  p.batch = batch;
+  p.n_max = n_max;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  p.head_dim = head_dim;
+  p.words = GRAFT_MASK_WORDS(n_max);
+  p.q = q;
+  p.k_tree = k_tree;
+  p.v_tree = v_tree;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.max_blocks = max_blocks_per_seq;
+  p.prefix_len = prefix_len;
+  p.tree_mask = tree_mask;
+  p.n_nodes = n_nodes;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.out = out;
+  p.n_splits = pl.n_splits;
+  p.tiles_per_split = pl.tiles_per_split;
+  p.n_row_groups = pl.n_row_groups;
+  p.rows_per_group = pl.rows_per_group;
+  char *ws = static_cast<char *>(workspace);
+  p.part_o = pl.n_splits > 1 ? reinterpret_cast<float *>(ws) : nullptr;
+  p.part_ml = pl.n_splits > 1
+                  ? reinterpret_cast<float *>(ws + align_up(pl.part_o_bytes, 256))
+                  : nullptr;
+  if (pl.mfma)
+    launch_attention_bf16_mfma(p, stream);
+  else
+    launch_attention_wave(dtype, p, stream);
+  if ((st = check_launch("graft_tree_attention")) != GRAFT_OK) return st;
+  if (pl.n_splits > 1) {
+    launch_attention_combine(dtype, p, stream);
+    if ((st = check_launch("graft_tree_attention (combine)")) != GRAFT_OK) return st;
+  }
+  return GRAFT_OK;
+}
+
+// ------------------------------------------------------------------- accept
+size_t graft_accept_workspace_size(int32_t batch, int32_t n_max, int32_t vocab) {
+  if (batch < 0 || n_max < 1 || n_max > GRAFT_MAX_NODES || vocab < 1) return 0;
+  return align_up((size_t)batch * n_max * accept_chunks(vocab) * sizeof(unsigned long long),
+                  256);
+}
+
+graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab,
+                          const void *logits, const int32_t *tree_token,
+                          const int32_t *tree_parent, const uint32_t *tree_mask,
+                          const int32_t *n_nodes, int32_t *argmax, int32_t *accept_len,
+                          int32_t *path_nodes, int32_t *path_tokens, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(dtype == GRAFT_F32 || dtype == GRAFT_BF16, GRAFT_ERR_INVALID_ARG,
+          "graft_accept: unknown dtype %d", (int)dtype);
+  REQUIRE(batch >= 0 && batch <= 65535 && n_max >= 1 && n_max <= GRAFT_MAX_NODES,
+          GRAFT_ERR_INVALID_ARG, "graft_accept: batch/n_max out of range");
+  REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_accept: vocab < 1");
+  REQUIRE((long long)batch * n_max <= 65535, GRAFT_ERR_UNSUPPORTED,
+          "graft_accept: batch * n_max above 65535");
+  if (batch == 0) return GRAFT_OK;
+  REQUIRE(logits && tree_token && tree_parent && tree_mask && n_nodes && argmax &&
+              accept_len && path_nodes && path_tokens,
+          GRAFT_ERR_INVALID_ARG, "graft_accept: null device pointer");
+  const size_t need = graft_accept_workspace_size(batch, n_max, vocab);
+  REQUIRE(workspace && workspace_bytes >= need, GRAFT_ERR_WORKSPACE,
+          "graft_accept: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  AcceptParams p{};
+  p.batch = batch;
+  p.n_max = n_max;
+  p.vocab = vocab;
+  p.words = GRAFT_MASK_WORDS(n_max);
+  p.chunks = accept_chunks(vocab);
+  p.chunk_len = 16384;
+  p.logits = logits;
+  p.tree_token = tree_token;
+  p.tree_parent = tree_parent;
+  p.tree_mask = tree_mask;
+  p.n_nodes = n_nodes;
+  p.argmax = argmax;
+  p.accept_len = accept_len;
+  p.path_nodes = path_nodes;
+  p.path_tokens = path_tokens;
+  p.partial = static_cast<unsigned long long *>(workspace);
+  launch_accept(dtype, p, stream);
+  return check_launch("graft_accept");
+}
+
+// ---------------------------------------------------------------- adjacency
+static uint32_t update_capacity(long long max_transitions) {
+  uint32_t c = 64;
+  while ((long long)c < 2 * max_transitions) c <<= 1;
+  return c;
+}
+
+size_t graft_update_adjacency_workspace_size(int32_t n_paths, int32_t path_stride) {
+  if (n_paths < 0 || path_stride < 2) return update_layout(64).total;
+  const long long t = (long long)n_paths * (path_stride - 1);
+  if (t > (1LL << 28)) return 0;
+  return update_layout(update_capacity(t)).total;
+}
+
+graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t vocab,
+                                    int32_t top_s, int32_t n_paths, int32_t path_stride,
+                                    const int32_t *path_tokens, const int32_t *accept_len,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_update_adjacency: vocab < 1");
+  REQUIRE(top_s >= 1 && top_s <= GRAFT_MAX_TOP_S, GRAFT_ERR_INVALID_ARG,
+          "graft_update_adjacency: top_s outside 1..%d", GRAFT_MAX_TOP_S);
+  REQUIRE(n_paths >= 0 && path_stride >= 0, GRAFT_ERR_INVALID_ARG,
+          "graft_update_adjacency: negative n_paths or path_stride");
+  const long long t = path_stride >= 2 ? (long long)n_paths * (path_stride - 1) : 0;
+  REQUIRE(t <= (1LL << 28), GRAFT_ERR_UNSUPPORTED,
+          "graft_update_adjacency: more than 2^28 transitions");
+  if (t == 0) return GRAFT_OK;
+  REQUIRE(m_ids && m_scores && path_tokens && accept_len, GRAFT_ERR_INVALID_ARG,
+          "graft_update_adjacency: null device pointer");
+  REQUIRE(workspace, GRAFT_ERR_WORKSPACE, "graft_update_adjacency: workspace is null");
+  // The layout depends only on the workspace size, so one zero-filled
+  // buffer stays valid across calls of different sizes.
+  uint32_t cap = 64;
+  while (update_layout(cap * 2).total <= workspace_bytes && cap < (1u << 30)) cap *= 2;
+  REQUIRE(update_layout(cap).total <= workspace_bytes && (long long)cap >= 2 * t,
+          GRAFT_ERR_WORKSPACE, "graft_update_adjacency: workspace of %zu bytes needed, %zu given",
+          graft_update_adjacency_workspace_size(n_paths, path_stride), workspace_bytes);
+  UpdateParams p{};
+  p.m_ids = m_ids;
+  p.m_scores = m_scores;
+  p.vocab = vocab;
+  p.top_s = top_s;
+  p.n_paths = n_paths;
+  p.path_stride = path_stride;
+  p.max_transitions = (int32_t)t;
+  p.path_tokens = path_tokens;
+  p.accept_len = accept_len;
+  p.ws = static_cast<char *>(workspace);
+  p.lay = update_layout(cap);
+  launch_update(p, stream);
+  return check_launch("graft_update_adjacency");
+}
+
+}  // extern "C"

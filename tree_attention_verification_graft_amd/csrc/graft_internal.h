@@ -1,0 +1,112 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/graft.h"
+
+namespace graft {
+
+// Thread-local error message behind graft_last_error().
+graft_status set_error(graft_status code, const char *fmt, ...);
+
+// Map the last HIP launch error (if any) to a status.
+graft_status check_launch(const char *what);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- tree build
+struct BuildParams {
+  graft_tree_config cfg;
+  int32_t batch, n_draft_max, vocab, top_s, n_max, words;
+  const int32_t *draft_parent;
+  const int32_t *draft_token;
+  const float *draft_conf;
+  const int32_t *n_draft;
+  const int32_t *root_token;
+  const int32_t *prefix_len;
+  const int32_t *m_ids;
+  int32_t *tree_token;
+  int32_t *tree_parent;
+  int32_t *tree_pos;
+  uint32_t *tree_mask;
+  int32_t *n_nodes;
+  int32_t *stage_out;
+};
+void launch_build_tree(const BuildParams &p, hipStream_t stream);
+
+// ----------------------------------------------------------------- attention
+struct AttnParams {
+  int32_t batch, n_max, hq, hkv, group, head_dim, words;
+  const void *q;
+  const void *k_tree;
+  const void *v_tree;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_table;
+  int32_t max_blocks;
+  const int32_t *prefix_len;
+  const uint32_t *tree_mask;
+  const int32_t *n_nodes;
+  float scale_log2;  // scale * log2(e)
+  void *out;
+  // split-K plan
+  int32_t n_splits;        // prefix splits per (sequence, kv head, row group)
+  int32_t tiles_per_split; // 64-key prefix tiles per split
+  int32_t n_row_groups;    // row groups per (sequence, kv head)
+  int32_t rows_per_group;  // query rows per group (multiple of 16)
+  float *part_o;           // [batch][hkv][groups][splits][rows][D]
+  float *part_ml;          // [batch][hkv][groups][splits][rows][2]
+};
+struct AttnPlan {
+  bool mfma;
+  int32_t n_splits, tiles_per_split, n_row_groups, rows_per_group;
+  size_t part_o_bytes, part_ml_bytes;
+};
+AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hq,
+                        int32_t hkv, int32_t head_dim, int32_t max_prefix);
+void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream);
+void launch_attention_wave(graft_dtype dtype, const AttnParams &p, hipStream_t stream);
+void launch_attention_combine(graft_dtype dtype, const AttnParams &p,
+                              hipStream_t stream);
+
+// -------------------------------------------------------------------- accept
+struct AcceptParams {
+  int32_t batch, n_max, vocab, words, chunks, chunk_len;
+  const void *logits;
+  const int32_t *tree_token;
+  const int32_t *tree_parent;
+  const uint32_t *tree_mask;
+  const int32_t *n_nodes;
+  int32_t *argmax;
+  int32_t *accept_len;
+  int32_t *path_nodes;
+  int32_t *path_tokens;
+  unsigned long long *partial;  // [batch * n_max][chunks] packed (value, ~index)
+};
+int32_t accept_chunks(int32_t vocab);
+void launch_accept(graft_dtype dtype, const AcceptParams &p, hipStream_t stream);
+
+// ---------------------------------------------------------------- adjacency
+struct UpdateLayout {
+  uint32_t capacity;        // hash slots (power of two)
+  size_t off_pair_key, off_pair_cnt, off_row_key, off_row_nnew, off_row_off,
+      off_row_fill, off_pair_list, off_row_list, off_bucket_v, off_bucket_c,
+      off_counters, total;
+};
+UpdateLayout update_layout(uint32_t capacity);
+struct UpdateParams {
+  int32_t *m_ids;
+  float *m_scores;
+  int32_t vocab, top_s, n_paths, path_stride, max_transitions;
+  const int32_t *path_tokens;
+  const int32_t *accept_len;
+  char *ws;
+  UpdateLayout lay;
+};
+void launch_update(const UpdateParams &p, hipStream_t stream);
+
+}  // namespace graft
