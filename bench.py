@@ -1,0 +1,265 @@
+"""Benchmark one prune-then-graft decode step on one MI355X.
+
+A step is the whole hot path over one batch: graft_build_tree ->
+graft_tree_attention -> graft_accept -> graft_update_adjacency, on inputs
+already resident in HBM.  Input sets rotate so that the live footprint
+exceeds the 256 MB Infinity Cache.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tree tokens/s + tree-attn KV-read HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_CONFIG = "llama3_8b_b1"   # the Llama-3-8B verify layer, batch 1
+ROTATE_BYTES = 600 << 20          # rotate input sets beyond the 256 MB MALL
+ATTN_SRC = os.path.join(ROOT, "tree_attention_verification_graft_amd", "csrc",
+                        "tree_attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attention_bytes(w, n_nodes):
+    """Algorithmic bytes of one attention launch: every prefix K and V row
+    once, every tree node's K and V once, q read once, out written once."""
+    e = 2 if w.dtype == "bf16" else 4
+    kv_prefix = int(w.prefix_len.sum()) * w.Hkv * w.D * 2 * e
+    kv_tree = int(np.sum(n_nodes)) * w.Hkv * w.D * 2 * e
+    q_out = int(np.sum(n_nodes)) * w.Hq * w.D * 2 * e
+    return kv_prefix + kv_tree, q_out
+
+
+def kernel_source_sha():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per attention launch from the committed counter summary,
+    or None when none exists for this workload and kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(name)
+    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """Time the oracle on a bounded sample of the same workload with one
+    host thread; scale to tokens/s."""
+    import oracle as O
+    import workloads as W
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        m_ids, m_scores = w.m_ids, w.m_scores
+        if w.prompt is not None:
+            m_ids, m_scores = O.update_adjacency(m_ids, m_scores, w.prompt[None],
+                                                 np.array([len(w.prompt) - 2]))
+        t1 = time.perf_counter()
+        tree = O.build_tree(w.cfg, w.draft_parent, w.draft_token, w.draft_conf, w.n_draft,
+                            w.root_token, w.prefix_len, m_ids)
+        t_build = time.perf_counter() - t1
+        logits = W.plant_path(w.logits, w.dtype, tree["token"], tree["parent"],
+                              tree["n_nodes"], w.plant_seed)
+        rows = [(b, i, h) for b in range(w.B) for i in range(int(tree["n_nodes"][b]))
+                for h in range(w.Hq)]
+        # attention: time rows until the budget is half spent, then scale
+        f64 = lambda a: O.as_f64(a, w.dtype)
+        args = [f64(w.q), f64(w.k_tree), f64(w.v_tree), f64(w.k_cache), f64(w.v_cache)]
+        rng = np.random.default_rng(0)
+        order = rng.permutation(len(rows))
+        done = 0
+        t2 = time.perf_counter()
+        chunk = 32
+        while done < len(rows) and time.perf_counter() - t2 < budget_s / 2:
+            sel = [rows[k] for k in order[done:done + chunk]]
+            O.tree_attention(*args, w.block_table, w.prefix_len, tree["mask"],
+                             tree["n_nodes"], w.scale, rows=sel)
+            done += len(sel)
+        t_attn = (time.perf_counter() - t2) * len(rows) / done
+        t3 = time.perf_counter()
+        acc = O.accept(logits, w.dtype, tree["token"], tree["parent"], tree["n_nodes"])
+        t_acc = time.perf_counter() - t3
+        t4 = time.perf_counter()
+        O.update_adjacency(m_ids, m_scores, acc["path_tokens"], acc["accept_len"])
+        t_upd = time.perf_counter() - t4
+    step = t_build + t_attn + t_acc + t_upd
+    tokens = int(tree["n_nodes"].sum())
+    return {
+        "value": tokens / step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": (f"one step of {w.name}: build, accept and update in full; attention on "
+                   f"{done} of {len(rows)} (node, head) rows, time scaled to all rows; "
+                   f"numpy float64, one thread"),
+        "seconds_per_step": step,
+        "components_s": {"build": t_build, "attention": t_attn, "accept": t_acc,
+                         "update": t_upd},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from tree_attention_verification_graft_amd.pipeline import DeviceStep, to_host
+
+    dev = torch.device("cuda:0")
+    log(f"generating workload {args.config}")
+    w = W.make(args.config)
+    from tree_attention_verification_graft_amd.binding import graft_version
+    log(graft_version())
+
+    # First set: seed M from the prompt if the workload has one, build once to
+    # plant an acceptable path into the stand-in logits.
+    base = DeviceStep(w, device=dev, alloc_update_for_prompt=True)
+    if w.prompt is not None:
+        base.seed_from_prompt(w.prompt)
+    base.build()
+    torch.cuda.synchronize()
+    t = base.tree_host()
+    logits = W.plant_path(w.logits, w.dtype, t["token"], t["parent"], t["n_nodes"],
+                          w.plant_seed)
+    base.logits.copy_(torch.from_numpy(logits.view(np.int16) if logits.dtype == np.uint16
+                                       else logits).to(dev).view(base.logits.dtype))
+    per_set = sum(x.numel() * x.element_size() for x in
+                  (base.q, base.k_tree, base.v_tree, base.k_cache, base.v_cache, base.logits))
+    n_sets = max(1, math.ceil(ROTATE_BYTES / per_set))
+    sets = [base]
+    for _ in range(n_sets - 1):
+        s = DeviceStep.__new__(DeviceStep)
+        s.__dict__.update(base.__dict__)
+        for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache", "logits"):
+            setattr(s, k, getattr(base, k).clone())
+        for k in ("tree_token", "tree_parent", "tree_pos", "tree_mask", "n_nodes", "stage",
+                  "out", "argmax", "accept_len", "path_nodes", "path_tokens"):
+            setattr(s, k, torch.empty_like(getattr(base, k)))
+        sets.append(s)
+    log(f"{n_sets} rotating input sets of {per_set / 2**20:.1f} MiB")
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def run(k, timed):
+        s = sets[k % n_sets]
+        if not timed:
+            s.step()
+            return None
+        e = [ev() for _ in range(5)]
+        e[0].record(stream)
+        s.build()
+        e[1].record(stream)
+        s.attention()
+        e[2].record(stream)
+        s.accept()
+        e[3].record(stream)
+        s.update()
+        e[4].record(stream)
+        return e
+
+    for k in range(args.warmup):
+        run(k, False)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    # whole-step throughput: no events inside the timed region
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        run(k, False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-call durations with HIP events on the launch stream
+    evs = [run(k, True) for k in range(args.steps)]
+    torch.cuda.synchronize()
+    comp = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
+    comp_ms = comp.mean(axis=0)
+
+    n_nodes = np.stack([to_host(s.n_nodes) for s in sets])
+    tokens = float(n_nodes.sum(axis=1).mean())
+    value = tokens / (ms_per_step / 1e3)
+    kv_bytes, qo_bytes = attention_bytes(w, n_nodes[0])
+    t_attn_s = comp_ms[1] / 1e3
+    achieved = (kv_bytes + qo_bytes) / t_attn_s / 1e9
+    kv_gbps = kv_bytes / t_attn_s / 1e9
+    traffic = measured_traffic(w.name)
+    log(f"step {ms_per_step * 1e3:.1f} us; build {comp_ms[0] * 1e3:.1f} attn "
+        f"{comp_ms[1] * 1e3:.1f} accept {comp_ms[2] * 1e3:.1f} update "
+        f"{comp_ms[3] * 1e3:.1f} us; attention {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "prefix_len_total": int(w.prefix_len.sum()),
+                   "kmax": w.kmax, "vocab": w.V, "top_s": w.S, "page": w.block,
+                   "rotating_sets": n_sets},
+        "kv_read_GBps": kv_gbps,
+        "kv_read_pct_of_peak": 100.0 * kv_gbps / HBM_PEAK_GBPS,
+        "components_us": {"build": comp_ms[0] * 1e3, "attention": comp_ms[1] * 1e3,
+                          "accept": comp_ms[2] * 1e3, "update": comp_ms[3] * 1e3},
+        "roofline": {
+            "kernel": "graft_tree_attention",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes + qo_bytes,
+            "launch_us": comp_ms[1] * 1e3,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (one thread)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

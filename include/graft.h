@@ -225,9 +225,12 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max,
  * m_ids int32 [vocab][top_s], m_scores float [vocab][top_s] (updated in
  * place); path_tokens int32 [n_paths][path_stride]; accept_len int32 [n_paths].
  * workspace: >= graft_update_adjacency_workspace_size(n_paths, path_stride)
- * bytes.  It must be zero-filled before its first use; every call leaves it
- * zero-filled again, so a workspace can be reused across calls without
- * clearing.  Calls that share one workspace must not overlap.
+ * bytes.  It must be zero-filled before its first use.  Every call leaves
+ * its hash tables and counters cleared again (the rest of the workspace is
+ * scratch that is written before it is read), so one workspace can be
+ * reused across calls of any size it covers without clearing.  Its layout
+ * depends only on workspace_bytes.  Calls that share one workspace must not
+ * overlap.
  */
 size_t graft_update_adjacency_workspace_size(int32_t n_paths, int32_t path_stride);
 graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t vocab,
