@@ -15,7 +15,12 @@ import workloads as W
 
 pytestmark = pytest.mark.gpu
 
+# Attention tolerance: 1e-2 (bf16 inputs, fp32 accumulation) or 1e-4 (fp32)
+# on top of the rounding of the output itself to its storage type, whose
+# relative error is at most half a unit in the last place (2^-9 for bf16,
+# 2^-24 for fp32).
 TOL = {"bf16": 1e-2, "f32": 1e-4}
+OUT_ROUND = {"bf16": 2.0 ** -9, "f32": 2.0 ** -24}
 
 
 def _say(msg):
@@ -52,7 +57,11 @@ def check_attention(w, out_gpu, tree, rows=None):
         rows = [(b, i, h) for b in range(w.B) for i in range(int(tree["n_nodes"][b]))
                 for h in range(w.Hq)]
     err = max(float(np.abs(got[b, i, h] - ref[b, i, h]).max()) for (b, i, h) in rows)
-    assert np.isfinite(err) and err <= TOL[w.dtype], f"attention max-abs {err}"
+    excess = max(float((np.abs(got[b, i, h] - ref[b, i, h])
+                        - OUT_ROUND[w.dtype] * np.abs(ref[b, i, h])).max())
+                 for (b, i, h) in rows)
+    assert np.isfinite(err) and excess <= TOL[w.dtype], (
+        f"attention max-abs {err} (beyond output rounding: {excess})")
     return err
 
 

@@ -72,10 +72,10 @@ def make_config(cfg: dict) -> TreeConfig:
     return c
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
     P, I, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {
         "graft_build_tree": [ctypes.POINTER(TreeConfig), I, I, P, P, P, P, P, P, P, I, I,

@@ -34,15 +34,39 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;           // head dim of the matrix-core path
 constexpr int kTile = 64;         // keys per LDS tile
 constexpr int kBlock = 16;        // tokens per KV page
-constexpr int kKStride = kD + 8;  // LDS row stride of the K tile (elements)
-constexpr int kVStride = kTile + 8;  // LDS row stride of the V^T tile (elements)
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, below any score
 constexpr int kThreads = 256;      // wavefront path
 constexpr int kMfmaWaves = 8;      // matrix-core path: 2 waves per SIMD
 constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kMaxNB = 3;          // 16-row blocks per wave
+constexpr int kMaxSplitPages = 1024;  // page-table slice held in LDS per split
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 row-swap permutes, which stay in the vector ALU.
+__device__ inline float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float s1 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s1), __float_as_uint(s1), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The running maximum used as the exponent offset is only moved when a new
+// score exceeds it by more than 2^kRescaleLog2; until then probabilities up
+// to 2^8 are accumulated as they are (exact softmax either way, since the
+// accumulator and the row sum share the offset), which saves most rescales.
+constexpr float kRescaleLog2 = 8.f;
 
 // LDS row of the K tile that holds key `k` (0..63) of the tile.  Rows are in
 // the order the transposed score blocks use: score block kb = 2*kp + half,
@@ -68,72 +92,102 @@ __device__ inline void load_mask4(uint32_t (&mw)[4], const uint32_t *src, int wo
   mw[3] = words > 3 ? src[3] : 0u;
 }
 
-// Zero the bf16 lanes of a 16-byte chunk whose key index is >= limit; the
-// chunk covers keys first .. first+7.
-__device__ inline uint4 mask_v_chunk(uint4 v, int first, int limit) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int k0 = first + 2 * e;
-    if (k0 >= limit) w[e] &= 0x00000000u;
-    else if (k0 + 1 >= limit) w[e] &= 0x0000ffffu;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+
+// ---------------------------------------------------------------------------
+// Matrix-core path.
+//
+// LDS holds kStages tile buffers (K 16 KB + V 16 KB each) filled by
+// asynchronous global->LDS loads (global_load_lds_dwordx4: each lane's 16
+// bytes land at M0 + 16 * lane), so up to kStages - 1 tiles are in flight
+// while one is computed, without staging registers.  The loads are issued
+// from inline assembly so that the compiler does not serialise every LDS
+// read behind them; the kernel waits on vmcnt itself.  Every load
+// instruction reads one KV page (base address in SGPRs, 32-bit lane
+// offsets).  The K tile is unpadded and XOR-swizzled: row R (in the order
+// the transposed score blocks use) holds its 16-byte chunk c at position
+// c ^ (R & 15).  The V tile keeps the cache's dim-major pages as they are
+// (page p at 4 KB * p, dim row d at 32 bytes * d) except that the two
+// 8-key halves of a row swap places when bits 2 and 3 of d differ.  Both
+// make the 16 lanes of a matrix-operand read hit 16 distinct 16-byte bank
+// groups.  Each wave
+// issues exactly kDmaPerStage loads per stage (a page past the prefix is
+// redirected to the tile's first page and later masked), so vmcnt counts
+// stay exact.
+constexpr int kStages = 4;
+constexpr int kKBytes = kTile * kD * 2;  // 16 KB
+constexpr int kVBytes = kD * kTile * 2;  // 16 KB
+constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kDmaPerStage = 4;          // per wave: 2 K + 2 V instructions
+
+// Issue one asynchronous 16-byte-per-lane global->LDS load from
+// base + voffset (base wave-uniform, in SGPRs).  lds_base is the
+// wave-uniform LDS byte address of the 1 KB destination block.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voffset, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_base), "v"(voffset), "s"(base)
+      : "memory", "m0");
+}
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// Workgroup barrier that also orders LDS traffic for the compiler.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
-template <int NB>
-__global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 sK[kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[kD * kVStride];
+// Key (0..63) of the tile held in K-tile row R: the inverse of k_row_of_key.
+__device__ inline int key_of_krow(int R) {
+  const int kb = R >> 4, m = R & 15;
+  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
+}
 
-  const int split = blockIdx.x;
-  const int rg = blockIdx.y % p.n_row_groups;
-  const int h = blockIdx.y / p.n_row_groups;
-  const int b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n16 = lane & 15;
-  const int g4 = lane >> 4;
+// Byte offset of element (dim d, key) in a V tile.
+__device__ inline int v_lds_offset(int d, int key) {
+  return (key >> 4) * 4096 + d * 32 + ((((key >> 3) & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4) +
+         2 * (key & 7);
+}
 
-  // Clamp caller-supplied counts to the buffer bounds (documented
-  // preconditions; the clamp only keeps reads in bounds if they are broken).
-  const int n_nodes = min(max(p.n_nodes[b], 0), p.n_max);
-  const int P = min(max(p.prefix_len[b], 0), p.max_blocks * kBlock);
-  const int G = p.group;
-  const int rows_b = n_nodes * G;
-  const int row0 = rg * p.rows_per_group;
-  if (row0 >= rows_b) return;  // group past this sequence's rows
+// Per-workgroup context of the matrix-core kernel (wave-uniform values).
+struct MfmaCtx {
+  int b, h, rg, split, tid, lane, n16, g4, wave;
+  int n_nodes, P, G, rows_b, row0, n_pages_b, t_begin, n_pref, n_tree;
+  uint32_t lds0;  // LDS byte address of stage 0
+};
 
-  const int nt_prefix = (P + kTile - 1) / kTile;
-  const int t_begin = split * p.tiles_per_split;
-  const int t_end = min(t_begin + p.tiles_per_split, nt_prefix);
-  const int n_pref = max(0, t_end - t_begin);
-  const int n_tree = split == 0 ? (n_nodes + kTile - 1) / kTile : 0;
-  if (n_pref == 0 && n_tree == 0) return;  // empty split
-
+// One wave's share, specialised on the number NA of 16-row query blocks it
+// owns (wave-uniform), so that no matrix instruction sits behind a per-block
+// branch.  Every wave runs the same loads and barriers whatever NA is.
+template <int NA>
+__device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
+                                               uint8_t *smem, const int32_t *s_pages) {
+  constexpr int NQ = NA > 0 ? NA : 1;
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
   const __bf16 *k_cache = static_cast<const __bf16 *>(p.k_cache);
   const __bf16 *v_cache = static_cast<const __bf16 *>(p.v_cache);
-  const int32_t *table = p.block_table + (size_t)b * p.max_blocks;
+  const int tid = c.tid, lane = c.lane, n16 = c.n16, g4 = c.g4, wave = c.wave;
 
-  // ---- per-wave query blocks: block k of this wave covers rows
-  // row0 + 16*(wave + 8k) .. +15 of the (node, query head) row space.
-  bf16x8 qf[NB][4];
-  f32x4 o[NB][8];
-  float m_run[NB], l_run[NB];
-  int my_row[NB];
-  bool blk_on[NB];
+  // ---- query blocks: block k covers rows row0 + 16*(wave + 8k) .. +15
+  bf16x8 qf[NQ][4];
+  f32x4 o[NQ][8];
+  // Row sums come from the same bf16 probabilities the P V op consumes, via
+  // one more matrix op against a ones operand, so every element of l_acc
+  // holds the sum over all keys of the lane's query.
+  f32x4 l_acc[NQ];
+  float m_run[NQ];
+  auto row_of = [&](int k) { return c.row0 + 16 * (wave + kMfmaWaves * k) + n16; };
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    const int rl = 16 * (wave + kMfmaWaves * k);
-    blk_on[k] = rl < p.rows_per_group && row0 + rl < rows_b;
-    const int r = row0 + rl + n16;
-    my_row[k] = r;
-    const bool rv = blk_on[k] && r < rows_b && rl + n16 < p.rows_per_group;
-    const int node = rv ? r / G : 0;
-    const int hq = h * G + (rv ? r % G : 0);
-    const __bf16 *qrow = q + (((size_t)b * p.n_max + node) * p.hq + hq) * kD;
+  for (int k = 0; k < NA; ++k) {
+    const int r = row_of(k);
+    const bool rv = r < c.rows_b;
+    const int node = rv ? r / c.G : 0;
+    const int hq = c.h * c.G + (rv ? r % c.G : 0);
+    const __bf16 *qrow = q + (((size_t)c.b * p.n_max + node) * p.hq + hq) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 v = rv ? *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g4) : zero4();
@@ -142,45 +196,46 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[k][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[k] = kNegBig;
-    l_run[k] = 0.f;
+    l_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // Let the query loads land now, through a wait the compiler can see:
+  // otherwise it would wait for them (and for every tile load in flight
+  // behind them) at the first matrix op of each tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // ---- tile loaders (global -> registers -> LDS)
-  uint4 kreg[2], vreg[2];
-  auto load_prefix = [&](int tile) {
-    const int key0 = tile * kTile;
+  // ---- asynchronous loads of prefix tile `it` (local index) into stage `st`
+  const size_t kv_head = (size_t)p.hkv;
+  auto issue_prefix = [&](int it, int st) {
+    const int tile = c.t_begin + it;
+    const uint32_t sk = c.lds0 + st * kStageBytes;
+    const uint32_t sv = sk + kKBytes;
+    const int first = s_pages[it * 4];  // the tile's first page is always in range
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int c = tid + kMfmaThreads * r;
-      const int kl = c >> 4, dc = c & 15;
-      const int key = key0 + kl;
-      if (key < P) {
-        const int blk = table[key >> 4];
-        kreg[r] = *reinterpret_cast<const uint4 *>(
-            k_cache + (((size_t)blk * p.hkv + h) * kBlock + (key & 15)) * kD + dc * 8);
-      } else {
-        kreg[r] = zero4();
+      const int inst = wave + kMfmaWaves * r;  // 0..15, one 1 KB block each
+      // K: rows 4*inst .. +3 hold four keys of one page; lane -> row
+      // 4*inst + lane/16, chunk position lane%16
+      {
+        const int R = 4 * inst + (lane >> 4);
+        const int kl = key_of_krow(R);
+        const int pg = key_of_krow(4 * inst) >> 4;  // uniform
+        const int blk = __builtin_amdgcn_readfirstlane(
+            tile * 4 + pg < c.n_pages_b ? s_pages[it * 4 + pg] : first);
+        const __bf16 *base = k_cache + ((size_t)blk * kv_head + c.h) * (kBlock * kD);
+        const uint32_t off = (uint32_t)((kl & 15) * 256 + (((lane & 15) ^ (R & 15)) << 4));
+        dma16(base, off, sk + inst * 1024);
       }
-      const int pg = c >> 8, w = c & 255, d = w >> 1, half = w & 1;
-      const int first = key0 + 16 * pg + 8 * half;
-      if (key0 + 16 * pg < P) {
-        const int blk = table[(key0 >> 4) + pg];
-        uint4 v = *reinterpret_cast<const uint4 *>(
-            v_cache + (((size_t)blk * p.hkv + h) * kD + d) * kBlock + 8 * half);
-        vreg[r] = (first + 8 <= P) ? v : mask_v_chunk(v, first, P);
-      } else {
-        vreg[r] = zero4();
+      // V: page inst/4, dim rows 32*(inst%4) .. +31; lane -> dim row
+      // 32*(inst%4) + lane/2, half position lane%2
+      {
+        const int pg = inst >> 2;
+        const int blk = __builtin_amdgcn_readfirstlane(
+            tile * 4 + pg < c.n_pages_b ? s_pages[it * 4 + pg] : first);
+        const __bf16 *base = v_cache + ((size_t)blk * kv_head + c.h) * (kD * kBlock);
+        const int d = 32 * (inst & 3) + (lane >> 1);
+        const uint32_t off = (uint32_t)(d * 32 + (((lane & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4));
+        dma16(base, off, sv + inst * 1024);
       }
-    }
-  };
-  auto store_prefix = [&]() {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = tid + kMfmaThreads * r;
-      const int kl = c >> 4, dc = c & 15;
-      *reinterpret_cast<uint4 *>(&sK[k_row_of_key(kl) * kKStride + dc * 8]) = kreg[r];
-      const int pg = c >> 8, w = c & 255, d = w >> 1, half = w & 1;
-      *reinterpret_cast<uint4 *>(&sV[d * kVStride + 16 * pg + 8 * half]) = vreg[r];
     }
   };
 
@@ -188,141 +243,177 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   // Half kp covers score blocks 2kp (keys 32kp + 8g + i) and 2kp+1
   // (keys 32kp + 8g + 4 + i) of lane group g, which are exactly the eight
   // key slots lane group g feeds to the P V matrix op.
-  auto compute = [&](int key0, bool tree) {
-    const int limit = tree ? n_nodes : P;
-    uint32_t mw[NB][4];
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      mw[k][0] = mw[k][1] = mw[k][2] = mw[k][3] = 0u;
-      if (tree && blk_on[k]) {
-        const int r = my_row[k];
-        const int node = r < rows_b ? r / G : 0;
-        load_mask4(mw[k], p.tree_mask + ((size_t)b * p.n_max + node) * p.words, p.words);
-      }
-    }
-#pragma unroll
+  auto compute = [&](int st, int key0, bool tree) {
+    const uint8_t *sK = smem + st * kStageBytes;
+    const uint8_t *sV = sK + kKBytes;
+    const int limit = tree ? c.n_nodes : c.P;
+    const bool masked = tree || key0 + kTile > c.P;  // wave-uniform
+#pragma unroll 1
     for (int kp = 0; kp < 2; ++kp) {
-      f32x4 s[NB][2];
+      f32x4 s[NQ][2];
 #pragma unroll
-      for (int k = 0; k < NB; ++k) s[k][0] = s[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < NA; ++k) s[k][0] = s[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-              &sK[(16 * (2 * kp + hh) + n16) * kKStride + 32 * kk + 8 * g4]);
-#pragma unroll
-          for (int k = 0; k < NB; ++k)
-            if (blk_on[k])
-              s[k][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[k][kk], s[k][hh], 0, 0, 0);
-        }
-      }
-      bf16x8 pb[NB];
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        if (!blk_on[k]) continue;
-        float mx = kNegBig;
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 a[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 32 * kp + 8 * g4 + 4 * hh + i;
-            bool vis = key < limit;
-            if (tree) vis = vis && ((mask_word(mw[k], key >> 5) >> (key & 31)) & 1u);
-            const float x = vis ? s[k][hh][i] * p.scale_log2 : -INFINITY;
-            s[k][hh][i] = x;
-            mx = fmaxf(mx, x);
-          }
+          const int R = 16 * (2 * kp + hh) + n16;
+          a[hh] = *reinterpret_cast<const bf16x8 *>(
+              sK + R * 256 + (((4 * kk + g4) ^ n16) << 4));
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[k], mx);
-        const float alpha = fast_exp2(m_run[k] - m_new);
-        m_run[k] = m_new;
-        float rs = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int k = 0; k < NA; ++k)
+            s[k][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[hh], qf[k][kk], s[k][hh],
+                                                               0, 0, 0);
+      }
+      bf16x8 pb[NQ];
+#pragma unroll
+      for (int k = 0; k < NA; ++k) {
+        if (masked) {
+          uint32_t mw[4] = {0u, 0u, 0u, 0u};
+          if (tree) {
+            const int r = row_of(k);
+            const int node = r < c.rows_b ? r / c.G : 0;
+            load_mask4(mw, p.tree_mask + ((size_t)c.b * p.n_max + node) * p.words, p.words);
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 32 * kp + 8 * g4 + 4 * hh + i;
+              bool vis = key < limit;
+              if (tree) vis = vis && ((mask_word(mw, key >> 5) >> (key & 31)) & 1u);
+              s[k][hh][i] = vis ? s[k][hh][i] : -INFINITY;
+            }
+        }
+        // raw-score maximum of this half, then in log2 units
+        const float mx = group4_max(fmaxf(
+            fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3])),
+            fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3]))));
+        const float mxs = mx * p.scale_log2;
+        if (__ballot(mxs > m_run[k] + kRescaleLog2)) {
+          const float m_new = fmaxf(m_run[k], mxs);
+          const float alpha = fast_exp2(m_run[k] - m_new);
+          m_run[k] = m_new;
+          l_acc[k] *= alpha;
+#pragma unroll
+          for (int d = 0; d < 8; ++d) o[k][d] *= alpha;
+        }
+        const float neg_m = -m_run[k];
         bf16x8 v;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(s[k][hh][i] - m_new);
-            rs += e;
-            v[4 * hh + i] = (__bf16)e;
-          }
+          for (int i = 0; i < 4; ++i)
+            v[4 * hh + i] = (__bf16)fast_exp2(fmaf(s[k][hh][i], p.scale_log2, neg_m));
         pb[k] = v;
-        l_run[k] = l_run[k] * alpha + rs;
-        // rescale the accumulator only when some query's maximum moved
-        if (__ballot(alpha < 1.f)) {
-#pragma unroll
-          for (int d = 0; d < 8; ++d) o[k][d] *= alpha;
-        }
       }
+      if (NA > 0) {
+        bf16x8 ones;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-            &sV[(16 * d + n16) * kVStride + 32 * kp + 8 * g4]);
+        for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
 #pragma unroll
-        for (int k = 0; k < NB; ++k)
-          if (blk_on[k])
-            o[k][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[k], o[k][d], 0, 0, 0);
+        for (int k = 0; k < NA; ++k)
+          l_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], l_acc[k], 0, 0, 0);
+#pragma unroll
+        for (int d0 = 0; d0 < 8; d0 += 2) {
+          bf16x8 av[2];
+#pragma unroll
+          for (int dd = 0; dd < 2; ++dd) {
+            const int d = 16 * (d0 + dd) + n16;
+            av[dd] = *reinterpret_cast<const bf16x8 *>(
+                sV + (2 * kp + (g4 >> 1)) * 4096 + d * 32 +
+                (((g4 & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4));
+          }
+#pragma unroll
+          for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+            for (int k = 0; k < NA; ++k)
+              o[k][d0 + dd] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[dd], pb[k], o[k][d0 + dd], 0, 0, 0);
+        }
       }
     }
   };
 
-  // ---- prefix tiles, software-pipelined: the next tile's global loads are
-  // in flight while the current tile is computed.
-  if (n_pref > 0) load_prefix(t_begin);
-  for (int it = 0; it < n_pref; ++it) {
-    __syncthreads();
-    store_prefix();
-    __syncthreads();
-    if (it + 1 < n_pref) load_prefix(t_begin + it + 1);
-    compute((t_begin + it) * kTile, false);
+  // ---- prefix tiles through the stage ring
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < c.n_pref) issue_prefix(s, s);
+  for (int it = 0; it < c.n_pref; ++it) {
+    // stage `it` has landed once at most (loads issued after it) remain
+    const int after = min(c.n_pref - 1 - it, kStages - 2);
+    if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
+    else if (after == 1) wait_vmcnt<kDmaPerStage>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // every wave's loads for stage `it` are in LDS; stage it-1 is free
+    if (it + kStages - 1 < c.n_pref) issue_prefix(it + kStages - 1, (it + kStages - 1) % kStages);
+    const int st = it % kStages;
+    const int key0 = (c.t_begin + it) * kTile;
+    if (key0 + kTile > c.P) {
+      // values past the prefix may be anything: zero them so P = 0 times V
+      // stays 0 (keys are masked out of the scores separately)
+      uint8_t *sV = smem + st * kStageBytes + kKBytes;
+      const int valid = c.P - key0;
+      for (int e = tid; e < kD * kTile; e += kMfmaThreads) {
+        const int d = e >> 6, key = e & 63;
+        if (key >= valid) *reinterpret_cast<__bf16 *>(sV + v_lds_offset(d, key)) = (__bf16)0.f;
+      }
+      lds_barrier();
+    }
+    if (NA > 0) compute(st, key0, false);
   }
 
-  // ---- tree tiles (split 0 only): keys are the tree nodes themselves.
+  // ---- tree tiles (split 0 only): the keys are the tree nodes themselves.
   const __bf16 *k_tree = static_cast<const __bf16 *>(p.k_tree);
   const __bf16 *v_tree = static_cast<const __bf16 *>(p.v_tree);
-  for (int tt = 0; tt < n_tree; ++tt) {
+  for (int tt = 0; tt < c.n_tree; ++tt) {
     const int key0 = tt * kTile;
-    __syncthreads();
+    uint8_t *sK = smem;  // stage 0 (all prefix loads have completed)
+    uint8_t *sV = smem + kKBytes;
+    wait_vmcnt<0>();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int c = tid + kMfmaThreads * r;
-      const int kl = c >> 4, dc = c & 15;
+      const int ch = tid + kMfmaThreads * r;
+      const int kl = ch >> 4, dc = ch & 15;
       const int j = key0 + kl;
       uint4 kv = zero4(), vv = zero4();
-      if (j < n_nodes) {
-        const size_t base = (((size_t)b * p.n_max + j) * p.hkv + h) * kD + dc * 8;
+      if (j < c.n_nodes) {
+        const size_t base = (((size_t)c.b * p.n_max + j) * p.hkv + c.h) * kD + dc * 8;
         kv = *reinterpret_cast<const uint4 *>(k_tree + base);
         vv = *reinterpret_cast<const uint4 *>(v_tree + base);
       }
-      *reinterpret_cast<uint4 *>(&sK[k_row_of_key(kl) * kKStride + dc * 8]) = kv;
+      const int R = k_row_of_key(kl);
+      *reinterpret_cast<uint4 *>(sK + R * 256 + ((dc ^ (R & 15)) << 4)) = kv;
       const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sV[(dc * 8 + e) * kVStride + kl] = ve[e];
+      for (int e = 0; e < 8; ++e) {
+        const int d = dc * 8 + e;
+        *reinterpret_cast<__bf16 *>(sV + v_lds_offset(d, kl)) = ve[e];
+      }
     }
-    __syncthreads();
-    compute(key0, true);
+    lds_barrier();
+    if (NA > 0) compute(0, key0, true);
   }
 
   // ---- epilogue: finish the row sums across the four lane groups and
   // write either the output or this split's partials.
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    if (!blk_on[k]) continue;
-    float l = l_run[k];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int r = my_row[k];
-    const int rl = r - row0;
-    if (r >= rows_b || rl >= p.rows_per_group) continue;
+  for (int k = 0; k < NA; ++k) {
+    const float l = l_acc[k][0];
+    const int r = row_of(k);
+    if (r >= c.rows_b) continue;
+    const int rl = r - c.row0;
     if (p.n_splits == 1) {
       const float inv = 1.f / l;
-      const int node = r / G;
-      const int hq = h * G + r % G;
+      const int node = r / c.G;
+      const int hq = c.h * c.G + r % c.G;
       __hip_bfloat16 *out = static_cast<__hip_bfloat16 *>(p.out) +
-                            (((size_t)b * p.n_max + node) * p.hq + hq) * kD;
+                            (((size_t)c.b * p.n_max + node) * p.hq + hq) * kD;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         ushort4 w;
@@ -334,7 +425,7 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
       }
     } else {
       const size_t prow =
-          ((((size_t)b * p.hkv + h) * p.n_row_groups + rg) * p.n_splits + split) *
+          ((((size_t)c.b * p.hkv + c.h) * p.n_row_groups + c.rg) * p.n_splits + c.split) *
               p.rows_per_group + rl;
       float *po = p.part_o + prow * kD;
 #pragma unroll
@@ -346,6 +437,61 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
       }
     }
   }
+}
+
+template <int NB>
+__global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  __shared__ int32_t s_pages[kMaxSplitPages];
+
+  MfmaCtx c;
+  c.split = blockIdx.x;
+  c.rg = blockIdx.y % p.n_row_groups;
+  c.h = blockIdx.y / p.n_row_groups;
+  c.b = blockIdx.z;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  c.n16 = c.lane & 15;
+  c.g4 = c.lane >> 4;
+  c.lds0 = (uint32_t)(uintptr_t)smem;
+
+  // Clamp caller-supplied counts to the buffer bounds (documented
+  // preconditions; the clamp only keeps reads in bounds if they are broken).
+  c.n_nodes = min(max(p.n_nodes[c.b], 0), p.n_max);
+  c.P = min(max(p.prefix_len[c.b], 0), p.max_blocks * kBlock);
+  c.G = p.group;
+  c.rows_b = c.n_nodes * c.G;
+  c.row0 = c.rg * p.rows_per_group;
+  if (c.row0 >= c.rows_b) return;  // group past this sequence's rows
+
+  const int nt_prefix = (c.P + kTile - 1) / kTile;
+  c.n_pages_b = (c.P + kBlock - 1) / kBlock;
+  c.t_begin = c.split * p.tiles_per_split;
+  const int t_end = min(c.t_begin + p.tiles_per_split, nt_prefix);
+  c.n_pref = max(0, t_end - c.t_begin);
+  c.n_tree = c.split == 0 ? (c.n_nodes + kTile - 1) / kTile : 0;
+  if (c.n_pref == 0 && c.n_tree == 0) return;  // empty split
+
+  // this split's slice of the page table (entries past the prefix are never
+  // used as addresses)
+  const int32_t *table = p.block_table + (size_t)c.b * p.max_blocks;
+  const int page0 = c.t_begin * 4;
+  const int n_sp = min(c.n_pref * 4, c.n_pages_b - page0);
+  for (int i = c.tid; i < n_sp; i += kMfmaThreads) s_pages[i] = table[page0 + i];
+  lds_barrier();
+
+  // the wave's active 16-row blocks are k = 0 .. na-1
+  int na = 0;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int rl = 16 * (c.wave + kMfmaWaves * k);
+    if (rl < p.rows_per_group && c.row0 + rl < c.rows_b) na = k + 1;
+  }
+  if (NB >= 3 && na == 3) mfma_wave_body<3>(p, c, smem, s_pages);
+  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1)>(p, c, smem, s_pages);
+  else if (na == 1) mfma_wave_body<1>(p, c, smem, s_pages);
+  else mfma_wave_body<0>(p, c, smem, s_pages);
 }
 
 // ------------------------------------------------------------------------
@@ -475,8 +621,15 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------------
 // Combine: merge the prefix splits of one output row (log-sum-exp in base 2).
+// The row's per-split maxima and sums are staged in LDS once; each thread
+// then owns one head dim and sums the splits' partial outputs with
+// coalesced loads.
+constexpr int kMaxSplits = 256;
+
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams p) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_inv_l;
   const int hq = blockIdx.x;
   const int node = blockIdx.y;
   const int b = blockIdx.z;
@@ -491,23 +644,30 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams p) {
   const int active =
       min(p.n_splits, max(1, (nt_prefix + p.tiles_per_split - 1) / p.tiles_per_split));
   const size_t base = (((size_t)b * p.hkv + h) * p.n_row_groups + rg) * p.n_splits;
+  const size_t stride = (size_t)p.rows_per_group;  // partial rows between splits
+  const float *ml = p.part_ml + (base * stride + rl) * 2;
+  const float *po = p.part_o + (base * stride + rl) * p.head_dim;
 
+  for (int sp = threadIdx.x; sp < active; sp += blockDim.x) s_w[sp] = ml[sp * stride * 2];
+  __syncthreads();
   float M = kNegBig;
-  for (int s = 0; s < active; ++s)
-    M = fmaxf(M, p.part_ml[((base + s) * p.rows_per_group + rl) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < active; ++s) {
-    const size_t pr = (base + s) * p.rows_per_group + rl;
-    L += p.part_ml[pr * 2 + 1] * fast_exp2(p.part_ml[pr * 2] - M);
+  for (int sp = 0; sp < active; ++sp) M = fmaxf(M, s_w[sp]);
+  __syncthreads();
+  for (int sp = threadIdx.x; sp < active; sp += blockDim.x)
+    s_w[sp] = fast_exp2(ml[sp * stride * 2] - M);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float L = 0.f;
+    for (int sp = 0; sp < active; ++sp) L += ml[sp * stride * 2 + 1] * s_w[sp];
+    s_inv_l = 1.f / L;
   }
-  const float inv = 1.f / L;
+  __syncthreads();
+  const float inv = s_inv_l;
   T *out = static_cast<T *>(p.out) + (((size_t)b * p.n_max + node) * p.hq + hq) * p.head_dim;
   for (int d = threadIdx.x; d < p.head_dim; d += blockDim.x) {
     float acc = 0.f;
-    for (int s = 0; s < active; ++s) {
-      const size_t pr = (base + s) * p.rows_per_group + rl;
-      acc += p.part_o[pr * p.head_dim + d] * fast_exp2(p.part_ml[pr * 2] - M);
-    }
+#pragma unroll 8
+    for (int sp = 0; sp < active; ++sp) acc += s_w[sp] * po[sp * stride * p.head_dim + d];
     out[d] = (T)(acc * inv);
   }
 }
@@ -545,7 +705,9 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
   int splits = (int)max(1L, min((long)tiles, (target + base - 1) / max(1L, base)));
   // keep splits at least 4 tiles long so partial traffic stays small
   splits = min(splits, max(1, tiles / 4));
+  splits = min(splits, kMaxSplits);
   pl.tiles_per_split = (tiles + splits - 1) / splits;
+  if (pl.mfma && pl.tiles_per_split * 4 > kMaxSplitPages) pl.tiles_per_split = kMaxSplitPages / 4;
   pl.n_splits = (tiles + pl.tiles_per_split - 1) / pl.tiles_per_split;
   const size_t prows = (size_t)batch * hkv * pl.n_row_groups * pl.n_splits * pl.rows_per_group;
   pl.part_o_bytes = pl.n_splits > 1 ? prows * head_dim * sizeof(float) : 0;
