@@ -195,7 +195,9 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
  *                   -1 padded; accept_len + 2 valid entries
  * Inputs: logits [batch][n_max][vocab] (dtype); tree arrays as produced by
  * graft_build_tree.
- * workspace: >= graft_accept_workspace_size(...) bytes, any contents.
+ * workspace: >= graft_accept_workspace_size(...) bytes, any contents (one
+ * packed value/index key per node row and 4096-entry vocabulary chunk).
+ * Calls that share one workspace must not overlap.
  */
 size_t graft_accept_workspace_size(int32_t batch, int32_t n_max, int32_t vocab);
 graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max,

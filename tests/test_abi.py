@@ -97,8 +97,9 @@ def test_accept_and_update_validation():
     assert acc(v=0) == -1
     assert acc(wsb=8) == -3
     assert acc(b=0) == 0
-    assert lib.graft_accept_workspace_size(2, 65, 151936) == 2 * 65 * 10 * 8 // 256 * 256 + (
-        256 if (2 * 65 * 10 * 8) % 256 else 0)
+    align = lambda x: -(-x // 256) * 256
+    # one packed (value, index) key per (row, 4096-wide vocab chunk)
+    assert lib.graft_accept_workspace_size(2, 65, 151936) == align(2 * 65 * 38 * 8)
     upd = lambda **k: lib.graft_update_adjacency(FAKE, FAKE, k.get("v", 100), k.get("s", 8),
                                                  k.get("np", 4), k.get("st", 10), FAKE, FAKE,
                                                  k.get("ws", FAKE), k.get("wsb", 1 << 20),

@@ -159,17 +159,21 @@ def test_edge_case(label, name, over):
 def test_update_reuses_one_workspace_and_is_deterministic():
     """Updates from the same state give bit-identical tables, and one
     zero-filled workspace serves successive calls of different sizes without
-    being cleared (each call matches the oracle)."""
+    being cleared (each call matches the oracle).  The sizes cover both the
+    per-step path (at most 4096 transitions) and the hash-table path, and the
+    Zipf-drawn paths give hub rows with more new successors than one wave
+    holds next to the row's S entries."""
     import torch
     from tree_attention_verification_graft_amd import binding as G
     from tree_attention_verification_graft_amd.pipeline import to_device, to_host
     rng = np.random.default_rng(3)
     V, S = 500, 8
     ids, sc = W.synth.seeded_adjacency(rng, V, S, W.Zipf(V))
-    ws = torch.zeros(G.graft_update_adjacency_workspace_size(40, 66), dtype=torch.uint8,
+    ws = torch.zeros(G.graft_update_adjacency_workspace_size(80, 66), dtype=torch.uint8,
                      device="cuda")
     results = {}
-    for rep, (n_paths, stride) in enumerate([(40, 66), (40, 66), (7, 20), (40, 66), (1, 2)]):
+    for rep, (n_paths, stride) in enumerate([(40, 66), (40, 66), (7, 20), (80, 66), (40, 66),
+                                             (1, 2), (80, 66)]):
         prng = np.random.default_rng(100 + n_paths)
         paths = W.Zipf(V).draw(prng, (n_paths, stride)).astype(np.int32)
         acc = prng.integers(-1, stride - 1, n_paths).astype(np.int32)

@@ -1,13 +1,17 @@
-// Greedy (lossless) acceptance of the verified hybrid tree.
+// Greedy (lossless) acceptance of the verified hybrid tree, in two launches.
 //
-// Stage 1 streams the logits: every (node row, vocab chunk) pair is one
-// workgroup that reduces its chunk to a packed 64-bit key whose high half is
-// an order-preserving image of the value (-0 folded onto +0) and whose low
-// half is the complemented index, so an unsigned max picks the largest value
-// and, among equal values, the lowest index.  Stage 2 (one workgroup per
-// sequence, one lane per node) finishes each row's argmax, marks the nodes
-// whose token equals their parent's argmax with wave ballots, keeps the nodes
-// whose whole ancestor mask is matched, and emits the deepest one's path.
+// argmax_chunks_kernel streams the logits: every (node row, 4096-entry vocab
+// chunk) pair is one workgroup whose threads issue all of their 16-byte loads
+// before reducing, so a launch keeps the whole live logits tensor in flight.
+// A chunk reduces to one packed 64-bit key whose high half is an
+// order-preserving image of the value (-0 folded onto +0) and whose low half
+// is the complemented index, so an unsigned max picks the largest value and,
+// among equal values, the lowest index.
+//
+// accept_path_kernel (one workgroup per sequence) folds the chunk keys of
+// every row with LDS atomics, marks the nodes whose token equals their
+// parent's argmax with wave ballots, keeps the nodes whose whole ancestor
+// mask is matched, and emits the deepest one's path.
 //
 // Method: "Draft Less, Retrieve More" (aitrends.kr summary), architecture
 // paragraph (lossless verification with retrieval nodes as proposals), read
@@ -20,11 +24,12 @@ namespace graft {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 16384;  // vocab entries per stage-1 workgroup
+constexpr int kChunk = 4096;      // vocab entries per argmax workgroup
+constexpr int kPathThreads = 256; // >= GRAFT_MAX_NODES
 
-__device__ inline uint32_t ord_bf16(uint16_t u) {
+__device__ inline uint32_t ord_bf16(uint32_t u) {
   if (u == 0x8000u) u = 0;  // -0 == +0
-  return (u & 0x8000u) ? (uint32_t)(~u & 0xffffu) : (uint32_t)(u | 0x8000u);
+  return (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
 }
 __device__ inline uint32_t ord_f32(uint32_t u) {
   if (u == 0x80000000u) u = 0;
@@ -37,10 +42,7 @@ __device__ inline unsigned long long umax64(unsigned long long a, unsigned long 
   return a > b ? a : b;
 }
 __device__ inline unsigned long long wave_max64(unsigned long long v) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const unsigned long long o = __shfl_xor(v, off);
-    v = umax64(v, o);
-  }
+  for (int off = 32; off > 0; off >>= 1) v = umax64(v, __shfl_xor(v, off));
   return v;
 }
 
@@ -50,40 +52,59 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(AcceptParams p)
   const int row = blockIdx.y;  // b * n_max + i
   const int b = row / p.n_max;
   const int i = row % p.n_max;
-  if (i >= p.n_nodes[b]) return;
-  const int lo = c * p.chunk_len;
-  const int hi = min(p.vocab, lo + p.chunk_len);
+  if (i >= p.n_nodes[b]) return;  // rows past the tree are not read
+  const int lo = c * kChunk;
+  const int hi = min(p.vocab, lo + kChunk);
   unsigned long long best = 0ull;
-  if (BF16) {
-    const uint16_t *x = static_cast<const uint16_t *>(p.logits) + (size_t)row * p.vocab;
-    if (VEC) {
-      // 8 values per 16-byte load; lo and hi are multiples of 8 here
-      for (int e = lo + 8 * threadIdx.x; e < hi; e += 8 * kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(x + e);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if (VEC) {
+    // 16-byte loads; lo and hi are multiples of the vector width here
+    constexpr int kPer = BF16 ? 8 : 4;                 // values per load
+    constexpr int kLoads = kChunk / (kPer * kThreads);  // 2 (bf16) or 4 (f32)
+    const uint4 *x = reinterpret_cast<const uint4 *>(
+        static_cast<const char *>(p.logits) + (size_t)row * p.vocab * (BF16 ? 2 : 4));
+    uint4 v[kLoads];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          best = umax64(best, pack(ord_bf16((uint16_t)(w[q] & 0xffffu)), e + 2 * q));
-          best = umax64(best, pack(ord_bf16((uint16_t)(w[q] >> 16)), e + 2 * q + 1));
+    for (int k = 0; k < kLoads; ++k) {
+      const int e = lo + (k * kThreads + threadIdx.x) * kPer;
+      v[k] = e < hi ? x[e / kPer] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int e = lo + (k * kThreads + threadIdx.x) * kPer;
+      if (e >= hi) continue;
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (BF16) {
+          best = umax64(best, pack(ord_bf16(w[q] & 0xffffu), e + 2 * q));
+          best = umax64(best, pack(ord_bf16(w[q] >> 16), e + 2 * q + 1));
+        } else {
+          best = umax64(best, pack(ord_f32(w[q]), e + q));
         }
       }
-    } else {
-      for (int e = lo + threadIdx.x; e < hi; e += kThreads)
-        best = umax64(best, pack(ord_bf16(x[e]), e));
     }
   } else {
-    const uint32_t *x = static_cast<const uint32_t *>(p.logits) + (size_t)row * p.vocab;
-    if (VEC) {
-      for (int e = lo + 4 * threadIdx.x; e < hi; e += 4 * kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(x + e);
-        best = umax64(best, pack(ord_f32(v.x), e));
-        best = umax64(best, pack(ord_f32(v.y), e + 1));
-        best = umax64(best, pack(ord_f32(v.z), e + 2));
-        best = umax64(best, pack(ord_f32(v.w), e + 3));
+    constexpr int kLoads = kChunk / kThreads;  // 16 scalar loads per thread
+    uint32_t v[kLoads];
+    if (BF16) {
+      const uint16_t *x = static_cast<const uint16_t *>(p.logits) + (size_t)row * p.vocab;
+#pragma unroll
+      for (int k = 0; k < kLoads; ++k) {
+        const int e = lo + k * kThreads + threadIdx.x;
+        v[k] = e < hi ? x[e] : 0u;
       }
     } else {
-      for (int e = lo + threadIdx.x; e < hi; e += kThreads)
-        best = umax64(best, pack(ord_f32(x[e]), e));
+      const uint32_t *x = static_cast<const uint32_t *>(p.logits) + (size_t)row * p.vocab;
+#pragma unroll
+      for (int k = 0; k < kLoads; ++k) {
+        const int e = lo + k * kThreads + threadIdx.x;
+        v[k] = e < hi ? x[e] : 0u;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int e = lo + k * kThreads + threadIdx.x;
+      if (e < hi) best = umax64(best, pack(BF16 ? ord_bf16(v[k]) : ord_f32(v[k]), e));
     }
   }
   __shared__ unsigned long long s_best[kThreads / 64];
@@ -97,40 +118,56 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(AcceptParams p)
   }
 }
 
-__global__ __launch_bounds__(GRAFT_MAX_NODES) void accept_path_kernel(AcceptParams p) {
+// Path selection, one workgroup per sequence; thread i owns node i.
+__global__ __launch_bounds__(kPathThreads) void accept_path_kernel(AcceptParams p) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const int lane = i & 63;
   const int wave = i >> 6;
-  const int n_nodes = p.n_nodes[b];
-  const bool live = i < n_nodes && i < p.n_max;
-
+  __shared__ unsigned long long s_key[GRAFT_MAX_NODES];
   __shared__ int32_t s_am[GRAFT_MAX_NODES];
+  __shared__ uint32_t s_mask[GRAFT_MAX_NODES][GRAFT_MAX_NODES / 32];
   __shared__ uint32_t s_match[GRAFT_MAX_NODES / 32];
   __shared__ uint32_t s_best[GRAFT_MAX_NODES / 64];
-  __shared__ uint32_t s_bestkey;
 
-  int am = -1;
-  if (live) {
-    unsigned long long m = 0ull;
-    const unsigned long long *part = p.partial + ((size_t)b * p.n_max + i) * p.chunks;
-    for (int c = 0; c < p.chunks; ++c) m = umax64(m, part[c]);
-    am = (int)(~(uint32_t)(m & 0xffffffffull));
+  // Every load below is independent of the others, so they are all in
+  // flight together.
+  const int n_nodes = p.n_nodes[b];
+  const size_t o = (size_t)b * p.n_max + i;
+  const bool in_row = i < p.n_max;
+  int par = -1, tok = -1;
+  uint32_t mw[4] = {0u, 0u, 0u, 0u};
+  if (in_row) {
+    par = p.tree_parent[o];
+    tok = p.tree_token[o];
+    const uint32_t *mrow = p.tree_mask + o * p.words;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mw[w] = w < p.words ? mrow[w] : 0u;
   }
-  s_am[i] = am;
-  if (i < p.n_max) p.argmax[(size_t)b * p.n_max + i] = am;
+  if (i < GRAFT_MAX_NODES) s_key[i] = 0ull;
+  __syncthreads();
+  // chunk keys of all rows, folded per row (rows past the tree are folded
+  // too and ignored below)
+  const int total = p.n_max * p.chunks;
+  const unsigned long long *part = p.partial + (size_t)b * total;
+#pragma unroll 4
+  for (int k = i; k < total; k += kPathThreads) atomicMax(&s_key[k / p.chunks], part[k]);
+  __syncthreads();
+
+  const bool live = in_row && i < n_nodes;
+  const int am = live ? (int)(~(uint32_t)(s_key[i] & 0xffffffffull)) : -1;
+  if (i < GRAFT_MAX_NODES) {
+    s_am[i] = am;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s_mask[i][w] = mw[w];
+  }
+  if (in_row) p.argmax[o] = am;
   __syncthreads();
 
   // match bit: the root always, else token == argmax of the parent's row
-  const size_t o = (size_t)b * p.n_max + i;
-  bool match = false;
-  int par = -1;
-  if (live) {
-    par = p.tree_parent[o];
-    match = (par < 0) || (par < i && p.tree_token[o] == s_am[par]);
-  }
+  const bool match = live && ((par < 0) || (par < i && tok == s_am[par]));
   const unsigned long long bal = __ballot(match);
-  if (lane == 0) {
+  if (lane == 0 && wave < GRAFT_MAX_NODES / 64) {
     s_match[2 * wave] = (uint32_t)(bal & 0xffffffffull);
     s_match[2 * wave + 1] = (uint32_t)(bal >> 32);
   }
@@ -138,13 +175,7 @@ __global__ __launch_bounds__(GRAFT_MAX_NODES) void accept_path_kernel(AcceptPara
 
   // fully matched: every ancestor-or-self bit is matched
   uint32_t key = 0u;
-  uint32_t mw[4] = {0u, 0u, 0u, 0u};
   if (live) {
-    const uint32_t *mrow = p.tree_mask + o * p.words;
-    mw[0] = p.words > 0 ? mrow[0] : 0u;
-    mw[1] = p.words > 1 ? mrow[1] : 0u;
-    mw[2] = p.words > 2 ? mrow[2] : 0u;
-    mw[3] = p.words > 3 ? mrow[3] : 0u;
     const bool full = ((mw[0] & s_match[0]) == mw[0]) && ((mw[1] & s_match[1]) == mw[1]) &&
                       ((mw[2] & s_match[2]) == mw[2]) && ((mw[3] & s_match[3]) == mw[3]);
     const int depth = __popc(mw[0]) + __popc(mw[1]) + __popc(mw[2]) + __popc(mw[3]) - 1;
@@ -156,39 +187,30 @@ __global__ __launch_bounds__(GRAFT_MAX_NODES) void accept_path_kernel(AcceptPara
     const uint32_t ok = __shfl_xor(wk, off);
     wk = ok > wk ? ok : wk;
   }
-  if (lane == 0) s_best[wave] = wk;
+  if (lane == 0 && wave < GRAFT_MAX_NODES / 64) s_best[wave] = wk;
   __syncthreads();
-  if (i == 0) {
-    uint32_t m = s_best[0];
-    for (int w = 1; w < GRAFT_MAX_NODES / 64; ++w) m = s_best[w] > m ? s_best[w] : m;
-    s_bestkey = m;
-  }
-  __syncthreads();
-  const uint32_t bk = s_bestkey;
+  uint32_t bk = s_best[0];
+  for (int w = 1; w < GRAFT_MAX_NODES / 64; ++w) bk = s_best[w] > bk ? s_best[w] : bk;
   // bk == 0 only when no node is live (n_nodes < 1 breaks the precondition):
   // fall back to the root so that every index below stays in bounds.
   const int best = bk ? 255 - (int)(bk & 0xffu) : 0;
   const int L = bk ? (int)(bk >> 8) - 1 : 0;  // accept length = depth of best
 
   // path = the best node's ancestor-or-self set in index order
-  __shared__ uint32_t s_path[4];
-  if (i == 0) {
-    const uint32_t *mrow = p.tree_mask + ((size_t)b * p.n_max + best) * p.words;
-    for (int w = 0; w < 4; ++w) s_path[w] = w < p.words ? mrow[w] : 0u;
-  }
-  __syncthreads();
   int32_t *pn = p.path_nodes + (size_t)b * p.n_max;
   int32_t *pt = p.path_tokens + (size_t)b * (p.n_max + 1);
-  if (live && ((s_path[i >> 5] >> (i & 31)) & 1u)) {
+  const uint32_t *path = s_mask[best];
+  const bool on_path = live && ((path[(i >> 5) & 3] >> (i & 31)) & 1u);
+  if (on_path) {
     int pos = 0;
-    for (int w = 0; w < (i >> 5); ++w) pos += __popc(s_path[w]);
-    pos += __popc(s_path[i >> 5] & ((1u << (i & 31)) - 1u));
+    for (int w = 0; w < (i >> 5); ++w) pos += __popc(path[w]);
+    pos += __popc(path[i >> 5] & ((1u << (i & 31)) - 1u));
     if (pos < p.n_max) {
       pn[pos] = i;
-      pt[pos] = p.tree_token[o];
+      pt[pos] = tok;
     }
   }
-  for (int k = i; k < p.n_max + 1; k += blockDim.x) {
+  for (int k = i; k < p.n_max + 1; k += kPathThreads) {
     if (k < p.n_max && k > L) pn[k] = -1;
     if (k > L + 1) pt[k] = -1;
   }
@@ -213,7 +235,7 @@ void launch_accept(graft_dtype dtype, const AcceptParams &p, hipStream_t stream)
     if (vec) hipLaunchKernelGGL((argmax_chunks_kernel<false, true>), g1, dim3(kThreads), 0, stream, p);
     else hipLaunchKernelGGL((argmax_chunks_kernel<false, false>), g1, dim3(kThreads), 0, stream, p);
   }
-  hipLaunchKernelGGL(accept_path_kernel, dim3(p.batch), dim3(GRAFT_MAX_NODES), 0, stream, p);
+  hipLaunchKernelGGL(accept_path_kernel, dim3(p.batch), dim3(kPathThreads), 0, stream, p);
 }
 
 }  // namespace graft

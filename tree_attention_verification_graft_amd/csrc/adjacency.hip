@@ -11,11 +11,17 @@
 // depend on the order in which atomics land.  Each kernel clears the
 // workspace entries it consumed, so the workspace is all-zero between calls.
 //
+// Calls with at most 4096 potential transitions (one decode step) take a
+// path that sorts the pairs in LDS instead and needs no workspace; both
+// paths give the same table.
+//
 // Method: "Draft Less, Retrieve More" (aitrends.kr summary), method paragraph
 // (fourth step: online update of M from the verified tree; fifth step:
 // prompt evidence for long contexts, which is the same update over the
 // prompt) and architecture paragraph.
 #include "graft_internal.h"
+
+#include <algorithm>
 
 namespace graft {
 namespace {
@@ -195,89 +201,296 @@ __device__ inline uint32_t score_key(float f) {
 __device__ inline unsigned long long cand_key(float score, int id) {
   return ((unsigned long long)score_key(score) << 32) | (uint32_t)(~(uint32_t)id);
 }
+__device__ inline float key_score(unsigned long long k) {
+  const uint32_t sk = (uint32_t)(k >> 32);
+  return __uint_as_float((sk & 0x80000000u) ? (sk & 0x7fffffffu) : ~sk);
+}
+__device__ inline int key_id(unsigned long long k) { return (int)(~(uint32_t)(k & 0xffffffffull)); }
 
-// 4) per touched row: merge and re-select the top S (one wave per row).
-__global__ __launch_bounds__(kThreads) void reselect_kernel(UpdateParams p) {
-  Tables t = tables(p);
+// Per-wave LDS scratch of the row merge.
+struct RowScratch {
+  int32_t id[GRAFT_MAX_TOP_S];
+  float sc[GRAFT_MAX_TOP_S];
+  uint32_t add[GRAFT_MAX_TOP_S];
+  unsigned long long key[64];
+};
+
+// Merge row u of M (ids/sc, S entries) with n new successor entries and
+// re-select the top S by (score descending, id ascending); one wave.
+// get(e) returns {v, count, first}: entries with first == false repeat an
+// earlier entry and are ignored.  Distinct ids per row make the candidate
+// keys distinct, so ranks are a permutation.
+struct NewEntry {
+  int v;
+  uint32_t count;
+  bool first;
+};
+template <class Get>
+__device__ void merge_row(int32_t *ids, float *sc, int S, int n, const Get &get, RowScratch &w) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t idx = blockIdx.x * (kThreads / 64) + wave;
-  __shared__ int32_t s_id[kThreads / 64][GRAFT_MAX_TOP_S];
-  __shared__ float s_sc[kThreads / 64][GRAFT_MAX_TOP_S];
-  __shared__ uint32_t s_add[kThreads / 64][GRAFT_MAX_TOP_S];
-  if (idx >= t.counters[kSavedRows]) return;  // whole wave leaves together
-  const int S = p.top_s;
-  const uint32_t rs = t.row_list[idx];
-  const int u = t.row_key[rs] - 1;
-  const uint32_t n = t.row_nnew[rs];
-  const uint32_t off = t.row_off[rs];
-  int32_t *ids = p.m_ids + (size_t)u * S;
-  float *sc = p.m_scores + (size_t)u * S;
-
+  int my_id = -1;
+  float my_sc = 0.f;
   if (lane < S) {
-    s_id[wave][lane] = ids[lane];
-    s_sc[wave][lane] = sc[lane];
-    s_add[wave][lane] = 0u;
+    my_id = ids[lane];
+    my_sc = sc[lane];
+    w.id[lane] = my_id;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  // bucket entries that are already in the row add to that entry
-  for (uint32_t e = lane; e < n; e += 64) {
-    const int v = t.bucket_v[off + e];
-    for (int s = 0; s < S; ++s)
-      if (s_id[wave][s] == v) s_add[wave][s] = t.bucket_c[off + e];
-  }
-  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // S rounds of "best candidate strictly below the previous pick"
+  if (S + n <= 64) {
+    // One candidate per lane: lanes < S hold the row's entries, lanes S ..
+    // S + n - 1 the new entries; each candidate's output slot is its rank.
+    bool valid = false;
+    int id = -1;
+    float score = 0.f;
+    if (lane < S) {
+      id = my_id;
+      valid = id >= 0;
+      uint32_t add = 0u;
+      for (int e = 0; e < n; ++e) {
+        const NewEntry x = get(e);
+        if (x.first && x.v == id) add = x.count;
+      }
+      score = my_sc + (float)add;
+    } else if (lane < S + n) {
+      const NewEntry x = get(lane - S);
+      bool resident = false;
+      for (int q = 0; q < S; ++q) resident |= (w.id[q] == x.v);
+      valid = x.first && !resident;
+      id = x.v;
+      score = (float)x.count;
+    }
+    const unsigned long long key = valid ? cand_key(score, id) : 0ull;
+    w.key[lane] = key;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int rank = 0;
+    for (int k = 0; k < S + n; ++k) rank += (w.key[k] > key);
+    const int n_valid = __popcll(__ballot(valid));
+    if (valid && rank < S) {
+      ids[rank] = id;
+      sc[rank] = score;
+    }
+    if (lane >= n_valid && lane < S) {
+      ids[lane] = -1;
+      sc[lane] = 0.f;
+    }
+    return;
+  }
+
+  // Many new entries (prompt evidence on a frequent token): S rounds of
+  // "best candidate strictly below the previous pick".
+  if (lane < S) {
+    w.sc[lane] = my_sc;
+    w.add[lane] = 0u;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int e = lane; e < n; e += 64) {
+    const NewEntry x = get(e);
+    if (!x.first) continue;
+    for (int q = 0; q < S; ++q)
+      if (w.id[q] == x.v) w.add[q] = x.count;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   unsigned long long last = ~0ull;
   for (int r = 0; r < S; ++r) {
     unsigned long long best = 0ull;
-    for (int s = lane; s < S; s += 64) {
-      const int id = s_id[wave][s];
-      if (id < 0) continue;
-      const float score = s_sc[wave][s] + (float)s_add[wave][s];
-      const unsigned long long k = cand_key(score, id);
-      if (k < last && k > best) best = k;
+    if (lane < S && w.id[lane] >= 0) {
+      const unsigned long long k = cand_key(w.sc[lane] + (float)w.add[lane], w.id[lane]);
+      if (k < last) best = k;
     }
-    for (uint32_t e = lane; e < n; e += 64) {
-      const int v = t.bucket_v[off + e];
+    for (int e = lane; e < n; e += 64) {
+      const NewEntry x = get(e);
+      if (!x.first) continue;
       bool resident = false;
-      for (int s = 0; s < S; ++s) resident |= (s_id[wave][s] == v);
+      for (int q = 0; q < S; ++q) resident |= (w.id[q] == x.v);
       if (resident) continue;
-      const unsigned long long k = cand_key((float)t.bucket_c[off + e], v);
+      const unsigned long long k = cand_key((float)x.count, x.v);
       if (k < last && k > best) best = k;
     }
     for (int o = 32; o > 0; o >>= 1) {
       const unsigned long long y = __shfl_xor(best, o);
       best = y > best ? y : best;
     }
-    // write after all lanes have read the old row (s_id/s_sc live in LDS)
-    if (lane == r) {
-      if (best == 0ull) {
-        ids[r] = -1;
-        sc[r] = 0.f;
-      } else {
-        const uint32_t sk = (uint32_t)(best >> 32);
-        const uint32_t bits = (sk & 0x80000000u) ? (sk & 0x7fffffffu) : ~sk;
-        ids[r] = (int)(~(uint32_t)(best & 0xffffffffull));
-        sc[r] = __uint_as_float(bits);
-      }
+    // the old row lives in LDS, so writing slot r cannot disturb the reads
+    if (lane == 0) {
+      ids[r] = best ? key_id(best) : -1;
+      sc[r] = best ? key_score(best) : 0.f;
     }
-    last = best == 0ull ? 0ull : best;
     if (best == 0ull) {
-      for (int s = r + 1 + lane; s < S; s += 64) {
-        ids[s] = -1;
-        sc[s] = 0.f;
+      for (int q = r + 1 + lane; q < S; q += 64) {
+        ids[q] = -1;
+        sc[q] = 0.f;
       }
       break;
     }
+    last = best;
   }
+}
+
+// 4) per touched row: merge and re-select the top S (one wave per row).
+__global__ __launch_bounds__(kThreads) void reselect_kernel(UpdateParams p) {
+  Tables t = tables(p);
+  const int wave = threadIdx.x >> 6;
+  const uint32_t idx = blockIdx.x * (kThreads / 64) + wave;
+  __shared__ RowScratch s_w[kThreads / 64];
+  if (idx >= t.counters[kSavedRows]) return;  // whole wave leaves together
+  const int S = p.top_s;
+  const uint32_t rs = t.row_list[idx];
+  const int u = t.row_key[rs] - 1;
+  const uint32_t n = t.row_nnew[rs];
+  const uint32_t off = t.row_off[rs];
+  const int32_t *bv = t.bucket_v + off;
+  const uint32_t *bc = t.bucket_c + off;
+  merge_row(p.m_ids + (size_t)u * S, p.m_scores + (size_t)u * S, S, (int)n,
+            [&](int e) { return NewEntry{bv[e], bc[e], true}; }, s_w[wave]);
   // clear this row's table entries
-  if (lane == 0) {
+  if ((threadIdx.x & 63) == 0) {
     t.row_key[rs] = 0;
     t.row_nnew[rs] = 0u;
     t.row_off[rs] = 0u;
     t.row_fill[rs] = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small calls (at most kSmallT potential transitions, the per-step case).
+// Every workgroup of the launch gathers the valid (u, v) keys into LDS,
+// sorts them (equal pairs form runs whose length is the count; each row is
+// one segment) and numbers the rows in sorted order; workgroup g then merges
+// rows g, g + G, ... with one wave per row.  The row numbering depends only
+// on the sorted keys, so all workgroups agree on it, and the table needs no
+// workspace.
+constexpr int kSmallT = 4096;
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+
+__device__ inline void cas_pair(unsigned long long &a, unsigned long long &b, bool up) {
+  if ((a > b) == up) {
+    const unsigned long long t = a;
+    a = b;
+    b = t;
+  }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void update_small_kernel(UpdateParams p) {
+  __shared__ unsigned long long s_key[kSmallT];
+  __shared__ uint16_t s_row_beg[kSmallT + 1];  // row r spans [beg[r], beg[r + 1])
+  __shared__ uint32_t s_wave_cnt[kSmallWaves];
+  __shared__ RowScratch s_w[kSmallWaves];
+  __shared__ int s_nv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const unsigned long long kNone = ~0ull;
+
+  // 1) gather the valid (u, v) keys (in any order: they are sorted next)
+  if (tid == 0) s_nv = 0;
+  __syncthreads();
+  const int per = p.path_stride - 1;
+  for (int t0 = 0; t0 < p.max_transitions; t0 += kSmallThreads) {
+    const int t = t0 + tid;
+    unsigned long long key = kNone;
+    if (t < p.max_transitions) {
+      const int path = t / per, k = t % per;
+      const int L = p.accept_len[path];
+      if (L >= 0 && k <= L && L + 2 <= p.path_stride) {
+        const int u = p.path_tokens[(size_t)path * p.path_stride + k];
+        const int v = p.path_tokens[(size_t)path * p.path_stride + k + 1];
+        if (u >= 0 && u < p.vocab && v >= 0 && v < p.vocab)
+          key = ((unsigned long long)(uint32_t)u << 32) | (uint32_t)v;
+      }
+    }
+    if (key != kNone) s_key[atomicAdd(&s_nv, 1)] = key;
+  }
+  __syncthreads();
+  const int nv = s_nv;
+  if (nv == 0) return;
+  int n2 = 1;
+  while (n2 < nv) n2 <<= 1;
+
+  // 2) ascending bitonic sort of the n2 >= nv keys (padding sorts last)
+  if (n2 <= 64) {
+    if (wave == 0) {
+      unsigned long long x = lane < nv ? s_key[lane] : kNone;
+      for (int size = 2; size <= 64; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const unsigned long long y = __shfl_xor(x, stride);
+          const bool up = (lane & size) == 0;        // block direction
+          const bool lower = (lane & stride) == 0;   // this lane keeps the min if up
+          const bool take_min = lower == up;
+          x = take_min ? (y < x ? y : x) : (y > x ? y : x);
+        }
+      }
+      if (lane < nv) s_key[lane] = x;
+    }
+  } else {
+    for (int i = nv + tid; i < n2; i += kSmallThreads) s_key[i] = kNone;
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < n2 / 2; i += kSmallThreads) {
+          const int lo = 2 * i - (i & (stride - 1));
+          unsigned long long a = s_key[lo], b = s_key[lo + stride];
+          cas_pair(a, b, (lo & size) == 0);
+          s_key[lo] = a;
+          s_key[lo + stride] = b;
+        }
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3) number the rows: row r starts at the r-th position whose u differs
+  // from its predecessor (a block-wide scan of the start flags)
+  int carry = 0;
+  for (int base = 0; base < nv; base += kSmallThreads) {
+    const int i = base + tid;
+    const bool start = i < nv && (i == 0 || (s_key[i] >> 32) != (s_key[i - 1] >> 32));
+    const unsigned long long bal = __ballot(start);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave_cnt[wave] = (uint32_t)__popcll(bal);
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += (int)s_wave_cnt[w];
+    if (start) s_row_beg[before + below] = (uint16_t)i;
+    int total = 0;
+    for (int w = 0; w < kSmallWaves; ++w) total += (int)s_wave_cnt[w];
+    carry += total;
+    __syncthreads();
+  }
+  const int n_rows = carry;
+  if (tid == 0) s_row_beg[n_rows] = (uint16_t)nv;
+  __syncthreads();
+
+  // 4) rows g, g + G, ... of this workgroup, one wave each
+  const int S = p.top_s;
+  const int G = gridDim.x;
+  for (int r = blockIdx.x + G * wave; r < n_rows; r += G * kSmallWaves) {
+    const int beg = s_row_beg[r];
+    const int end = s_row_beg[r + 1];
+    const int u = (int)(s_key[beg] >> 32);
+    auto get = [&](int e) {
+      const int i = beg + e;
+      const unsigned long long k = s_key[i];
+      NewEntry x;
+      x.v = (int)(k & 0xffffffffull);
+      x.first = i == beg || s_key[i - 1] != k;
+      int j = i + 1;
+      if (x.first)
+        while (j < end && s_key[j] == k) ++j;
+      x.count = (uint32_t)(j - i);
+      return x;
+    };
+    merge_row(p.m_ids + (size_t)u * S, p.m_scores + (size_t)u * S, S, end - beg, get,
+              s_w[wave]);
   }
 }
 
@@ -309,13 +522,22 @@ UpdateLayout update_layout(uint32_t capacity) {
 }
 
 void launch_update(const UpdateParams &p, hipStream_t stream) {
+  if (p.max_transitions <= kSmallT) {
+    // enough workgroups that every touched row (at most one per transition)
+    // gets a wave of its own
+    const int groups = std::max(1, std::min(64, (p.max_transitions + kSmallWaves - 1) / kSmallWaves));
+    hipLaunchKernelGGL(update_small_kernel, dim3(groups), dim3(kSmallThreads), 0, stream, p);
+    return;
+  }
   const uint32_t half = p.lay.capacity / 2;
   const int g1 = (p.max_transitions + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(scatter_kernel, dim3(g1), dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, p);
-  hipLaunchKernelGGL(place_kernel, dim3((half + kThreads - 1) / kThreads), dim3(kThreads), 0,
+  // distinct pairs and touched rows are both at most max_transitions
+  const uint32_t most = std::min<uint32_t>(half, (uint32_t)p.max_transitions);
+  hipLaunchKernelGGL(place_kernel, dim3((most + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      stream, p);
-  hipLaunchKernelGGL(reselect_kernel, dim3((half + 3) / 4), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(reselect_kernel, dim3((most + 3) / 4), dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace graft

@@ -253,7 +253,6 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32
   p.vocab = vocab;
   p.words = GRAFT_MASK_WORDS(n_max);
   p.chunks = accept_chunks(vocab);
-  p.chunk_len = 16384;
   p.logits = logits;
   p.tree_token = tree_token;
   p.tree_parent = tree_parent;

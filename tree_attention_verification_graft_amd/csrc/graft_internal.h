@@ -75,7 +75,7 @@ void launch_attention_combine(graft_dtype dtype, const AttnParams &p,
 
 // -------------------------------------------------------------------- accept
 struct AcceptParams {
-  int32_t batch, n_max, vocab, words, chunks, chunk_len;
+  int32_t batch, n_max, vocab, words, chunks;
   const void *logits;
   const int32_t *tree_token;
   const int32_t *tree_parent;

@@ -23,6 +23,8 @@
 // row, keys spread over lanes for q.k, head dims over lanes for P V.
 #include <hip/hip_bf16.h>
 
+#include <algorithm>
+
 #include "graft_internal.h"
 
 namespace graft {
@@ -39,7 +41,6 @@ constexpr int kThreads = 256;      // wavefront path
 constexpr int kMfmaWaves = 8;      // matrix-core path: 2 waves per SIMD
 constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kMaxNB = 3;          // 16-row blocks per wave
-constexpr int kMaxSplitPages = 1024;  // page-table slice held in LDS per split
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -165,7 +166,7 @@ struct MfmaCtx {
 // branch.  Every wave runs the same loads and barriers whatever NA is.
 template <int NA>
 __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
-                                               uint8_t *smem, const int32_t *s_pages) {
+                                               uint8_t *smem) {
   constexpr int NQ = NA > 0 ? NA : 1;
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
   const __bf16 *k_cache = static_cast<const __bf16 *>(p.k_cache);
@@ -198,18 +199,32 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     m_run[k] = kNegBig;
     l_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Let the query loads land now, through a wait the compiler can see:
-  // otherwise it would wait for them (and for every tile load in flight
-  // behind them) at the first matrix op of each tile.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // ---- asynchronous loads of prefix tile `it` (local index) into stage `st`
+  // from its four pages `pg`.
   const size_t kv_head = (size_t)p.hkv;
-  auto issue_prefix = [&](int it, int st) {
-    const int tile = c.t_begin + it;
+  // The page table is read-only for the whole kernel: reading it through the
+  // constant address space lets uniform indices become scalar loads.
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32 *table = (const_i32 *)(p.block_table + (size_t)c.b * p.max_blocks);
+  // Unconditional scalar loads at clamped (uniform) indices: a page past
+  // the prefix becomes the sequence's last page, whose keys get masked.
+  const int last_page = max(c.n_pages_b - 1, 0);
+  auto tile_pages = [&](int it) {
+    const int pg0 = (c.t_begin + it) * 4;
+    int4 r;
+    r.x = table[__builtin_amdgcn_readfirstlane(min(pg0, last_page))];
+    r.y = table[__builtin_amdgcn_readfirstlane(min(pg0 + 1, last_page))];
+    r.z = table[__builtin_amdgcn_readfirstlane(min(pg0 + 2, last_page))];
+    r.w = table[__builtin_amdgcn_readfirstlane(min(pg0 + 3, last_page))];
+    return r;
+  };
+  auto page_of = [](const int4 &pg, int i) {
+    return i == 0 ? pg.x : i == 1 ? pg.y : i == 2 ? pg.z : pg.w;
+  };
+  auto issue_prefix = [&](int st, const int4 &pg) {
     const uint32_t sk = c.lds0 + st * kStageBytes;
     const uint32_t sv = sk + kKBytes;
-    const int first = s_pages[it * 4];  // the tile's first page is always in range
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int inst = wave + kMfmaWaves * r;  // 0..15, one 1 KB block each
@@ -218,9 +233,8 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       {
         const int R = 4 * inst + (lane >> 4);
         const int kl = key_of_krow(R);
-        const int pg = key_of_krow(4 * inst) >> 4;  // uniform
-        const int blk = __builtin_amdgcn_readfirstlane(
-            tile * 4 + pg < c.n_pages_b ? s_pages[it * 4 + pg] : first);
+        const int blk =
+            __builtin_amdgcn_readfirstlane(page_of(pg, key_of_krow(4 * inst) >> 4));
         const __bf16 *base = k_cache + ((size_t)blk * kv_head + c.h) * (kBlock * kD);
         const uint32_t off = (uint32_t)((kl & 15) * 256 + (((lane & 15) ^ (R & 15)) << 4));
         dma16(base, off, sk + inst * 1024);
@@ -228,12 +242,11 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       // V: page inst/4, dim rows 32*(inst%4) .. +31; lane -> dim row
       // 32*(inst%4) + lane/2, half position lane%2
       {
-        const int pg = inst >> 2;
-        const int blk = __builtin_amdgcn_readfirstlane(
-            tile * 4 + pg < c.n_pages_b ? s_pages[it * 4 + pg] : first);
+        const int blk = __builtin_amdgcn_readfirstlane(page_of(pg, inst >> 2));
         const __bf16 *base = v_cache + ((size_t)blk * kv_head + c.h) * (kD * kBlock);
         const int d = 32 * (inst & 3) + (lane >> 1);
-        const uint32_t off = (uint32_t)(d * 32 + (((lane & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4));
+        const uint32_t off =
+            (uint32_t)(d * 32 + (((lane & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4));
         dma16(base, off, sv + inst * 1024);
       }
     }
@@ -339,18 +352,29 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     }
   };
 
-  // ---- prefix tiles through the stage ring
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < c.n_pref) issue_prefix(s, s);
+  // ---- prefix tiles through the stage ring.  Prologue: the first two
+  // stages are issued behind the query loads and the wait for both is made
+  // visible to the compiler (otherwise it would drain every load in flight
+  // before the first matrix op of each tile); later stages are issued one
+  // tile ahead of use with page ids fetched by scalar loads a tile earlier.
+  int4 pages_next = make_int4(0, 0, 0, 0);
+  if (c.n_pref > 0) issue_prefix(0, tile_pages(0));
+  if (c.n_pref > 1) issue_prefix(1, tile_pages(1));
+  if (c.n_pref > 2) pages_next = tile_pages(2);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries and stages 0, 1
+  if (c.n_pref > 2) issue_prefix(2, pages_next);
+  if (c.n_pref > 3) pages_next = tile_pages(3);
   for (int it = 0; it < c.n_pref; ++it) {
-    // stage `it` has landed once at most (loads issued after it) remain
+    // stage `it` has landed once at most the loads issued after it remain
     const int after = min(c.n_pref - 1 - it, kStages - 2);
     if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
     else if (after == 1) wait_vmcnt<kDmaPerStage>();
     else wait_vmcnt<0>();
     lds_barrier();  // every wave's loads for stage `it` are in LDS; stage it-1 is free
-    if (it + kStages - 1 < c.n_pref) issue_prefix(it + kStages - 1, (it + kStages - 1) % kStages);
+    if (it + kStages - 1 < c.n_pref) {
+      issue_prefix((it + kStages - 1) % kStages, pages_next);
+      if (it + kStages < c.n_pref) pages_next = tile_pages(it + kStages);
+    }
     const int st = it % kStages;
     const int key0 = (c.t_begin + it) * kTile;
     if (key0 + kTile > c.P) {
@@ -442,13 +466,22 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
 template <int NB>
 __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
-  __shared__ int32_t s_pages[kMaxSplitPages];
 
+  // XCD-aware decode: workgroups are dispatched to the 8 XCDs round-robin,
+  // so id = xcd + 8 * slot.  The row groups of one KV stream (sequence,
+  // head, split) take consecutive slots on one XCD and share its L2.
   MfmaCtx c;
-  c.split = blockIdx.x;
-  c.rg = blockIdx.y % p.n_row_groups;
-  c.h = blockIdx.y / p.n_row_groups;
-  c.b = blockIdx.z;
+  {
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    c.rg = slot % p.n_row_groups;
+    const int cluster = (slot / p.n_row_groups) * 8 + xcd;
+    const int n_clusters = p.batch * p.hkv * p.n_splits;
+    if (cluster >= n_clusters) return;
+    c.split = cluster % p.n_splits;
+    c.h = (cluster / p.n_splits) % p.hkv;
+    c.b = cluster / (p.n_splits * p.hkv);
+  }
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
@@ -473,13 +506,6 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   c.n_tree = c.split == 0 ? (c.n_nodes + kTile - 1) / kTile : 0;
   if (c.n_pref == 0 && c.n_tree == 0) return;  // empty split
 
-  // this split's slice of the page table (entries past the prefix are never
-  // used as addresses)
-  const int32_t *table = p.block_table + (size_t)c.b * p.max_blocks;
-  const int page0 = c.t_begin * 4;
-  const int n_sp = min(c.n_pref * 4, c.n_pages_b - page0);
-  for (int i = c.tid; i < n_sp; i += kMfmaThreads) s_pages[i] = table[page0 + i];
-  lds_barrier();
 
   // the wave's active 16-row blocks are k = 0 .. na-1
   int na = 0;
@@ -488,10 +514,10 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
     const int rl = 16 * (c.wave + kMfmaWaves * k);
     if (rl < p.rows_per_group && c.row0 + rl < c.rows_b) na = k + 1;
   }
-  if (NB >= 3 && na == 3) mfma_wave_body<3>(p, c, smem, s_pages);
-  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1)>(p, c, smem, s_pages);
-  else if (na == 1) mfma_wave_body<1>(p, c, smem, s_pages);
-  else mfma_wave_body<0>(p, c, smem, s_pages);
+  if (NB >= 3 && na == 3) mfma_wave_body<3>(p, c, smem);
+  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1)>(p, c, smem);
+  else if (na == 1) mfma_wave_body<1>(p, c, smem);
+  else mfma_wave_body<0>(p, c, smem);
 }
 
 // ------------------------------------------------------------------------
@@ -621,19 +647,28 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------------
 // Combine: merge the prefix splits of one output row (log-sum-exp in base 2).
-// The row's per-split maxima and sums are staged in LDS once; each thread
-// then owns one head dim and sums the splits' partial outputs with
-// coalesced loads.
+// One wave per row, no barriers: lane s reads split s's (max, sum), the
+// wave reduces them, and each lane accumulates two head dims over the
+// splits, taking split j's weight from lane j with a scalar read-lane.
 constexpr int kMaxSplits = 256;
 
+__device__ inline float wave_max(float x) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 template <typename T>
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams p) {
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_inv_l;
-  const int hq = blockIdx.x;
-  const int node = blockIdx.y;
-  const int b = blockIdx.z;
-  if (node >= min(p.n_nodes[b], p.n_max)) return;
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int hq = (int)(row % p.hq);
+  const int node = (int)((row / p.hq) % p.n_max);
+  const int b = (int)(row / ((long)p.hq * p.n_max));
+  if (b >= p.batch || node >= min(p.n_nodes[b], p.n_max)) return;  // whole wave
   const int G = p.group;
   const int h = hq / G;
   const int r = node * G + hq % G;
@@ -647,38 +682,85 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnParams p) {
   const size_t stride = (size_t)p.rows_per_group;  // partial rows between splits
   const float *ml = p.part_ml + (base * stride + rl) * 2;
   const float *po = p.part_o + (base * stride + rl) * p.head_dim;
+  const int dpl = p.head_dim / 64;  // 1 or 2 dims per lane
 
-  for (int sp = threadIdx.x; sp < active; sp += blockDim.x) s_w[sp] = ml[sp * stride * 2];
-  __syncthreads();
   float M = kNegBig;
-  for (int sp = 0; sp < active; ++sp) M = fmaxf(M, s_w[sp]);
-  __syncthreads();
-  for (int sp = threadIdx.x; sp < active; sp += blockDim.x)
-    s_w[sp] = fast_exp2(ml[sp * stride * 2] - M);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float L = 0.f;
-    for (int sp = 0; sp < active; ++sp) L += ml[sp * stride * 2 + 1] * s_w[sp];
-    s_inv_l = 1.f / L;
+  for (int s0 = 0; s0 < active; s0 += 64)
+    if (s0 + lane < active) M = fmaxf(M, ml[(s0 + lane) * stride * 2]);
+  M = wave_max(M);
+  float L = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < active; s0 += 64) {
+    float w = 0.f;
+    if (s0 + lane < active) {
+      const float *e = ml + (s0 + lane) * stride * 2;
+      w = fast_exp2(e[0] - M);
+      L += w * e[1];
+    }
+    const int n = min(64, active - s0);
+    const size_t sstride = stride * p.head_dim;
+    const float *o0 = po + (size_t)s0 * sstride + dpl * lane;
+    int j = 0;
+    for (; j + 8 <= n; j += 8) {  // eight independent loads in flight
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = dpl == 2 ? *reinterpret_cast<const float2 *>(o0 + (size_t)(j + u) * sstride)
+                        : make_float2(o0[(size_t)(j + u) * sstride], 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
+        acc0 += wj * v[u].x;
+        acc1 += wj * v[u].y;
+      }
+    }
+    for (; j < n; ++j) {
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+      const float2 v = dpl == 2 ? *reinterpret_cast<const float2 *>(o0 + (size_t)j * sstride)
+                                : make_float2(o0[(size_t)j * sstride], 0.f);
+      acc0 += wj * v.x;
+      acc1 += wj * v.y;
+    }
   }
-  __syncthreads();
-  const float inv = s_inv_l;
+  const float inv = 1.f / wave_sum(L);
   T *out = static_cast<T *>(p.out) + (((size_t)b * p.n_max + node) * p.hq + hq) * p.head_dim;
-  for (int d = threadIdx.x; d < p.head_dim; d += blockDim.x) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int sp = 0; sp < active; ++sp) acc += s_w[sp] * po[sp * stride * p.head_dim + d];
-    out[d] = (T)(acc * inv);
+  if (dpl == 2) {
+    out[2 * lane] = (T)(acc0 * inv);
+    out[2 * lane + 1] = (T)(acc1 * inv);
+  } else {
+    out[lane] = (T)(acc0 * inv);
   }
 }
 
 }  // namespace
 
 // ------------------------------------------------------------------------
-// Launch planning.  Query rows per KV head are n_max * group; the matrix-core
-// path tiles them in blocks of 16, at most kMaxNB blocks per wave and
-// kMfmaWaves waves (384 rows per workgroup).  Prefix splits are sized so the grid holds about two
-// workgroups per compute unit.
+// Launch planning.  Query rows per KV head are n_max * group, in blocks of
+// 16.  The matrix-core path holds one workgroup per compute unit (its LDS
+// ring and registers fill one), so the plan picks the number of row groups
+// and prefix splits that minimise an estimate of
+//   rounds * tiles per workgroup * (blocks on the busiest SIMD)
+// plus a fill latency per round and, when the prefix is split, the split
+// partials' traffic through the combine.  The wavefront path splits the
+// prefix so the grid holds about two workgroups per compute unit.
+namespace {
+constexpr int kComputeUnits = 256;
+constexpr double kTileBlockUs = 34.0 * 16.0 / 2400.0 / 0.45;  // one 16-row block, one tile
+constexpr double kFillUs = 3.0;
+constexpr double kCombineBytesPerUs = 4.0e6;  // partial traffic through the combine
+constexpr double kL2BytesPerUs = 16.0e6;      // KV re-reads by extra row groups (L2)
+constexpr double kHbmBytesPerUs = 6.0e6;      // streaming reads from HBM
+
+int busiest_simd_blocks(int blocks_per_group) {
+  int best = 0;
+  for (int j = 0; j < 4; ++j) {  // SIMD j runs waves j and j + 4
+    const int a = max(0, (blocks_per_group - j + kMfmaWaves - 1) / kMfmaWaves);
+    const int b = max(0, (blocks_per_group - j - 4 + kMfmaWaves - 1) / kMfmaWaves);
+    best = max(best, a + b);
+  }
+  return best;
+}
+}  // namespace
+
 AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hq,
                         int32_t hkv, int32_t head_dim, int32_t max_prefix) {
   AttnPlan pl{};
@@ -686,29 +768,46 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
   const int rows = n_max * group;
   pl.mfma = dtype == GRAFT_BF16 && head_dim == kD && rows >= 16;
   const int tiles = max(1, (max_prefix + kTile - 1) / kTile);
-  int per_seq_groups;
   if (pl.mfma) {
     const int blocks = (rows + 15) / 16;
     const int per_group = kMfmaWaves * kMaxNB;
-    const int groups = (blocks + per_group - 1) / per_group;
-    const int blocks_per_group = (blocks + groups - 1) / groups;
-    pl.n_row_groups = groups;
-    pl.rows_per_group = 16 * blocks_per_group;
-    per_seq_groups = groups;
+    const int g_min = (blocks + per_group - 1) / per_group;
+    const double kv_bytes = (double)batch * hkv * tiles * kTile * kD * 2 * 2;
+    double best = 1e30;
+    for (int groups = g_min; groups <= min(blocks, 4 * g_min); ++groups) {
+      const int bpg = (blocks + groups - 1) / groups;
+      const int simd = busiest_simd_blocks(bpg);
+      for (int splits = 1; splits <= min(tiles, kMaxSplits); ++splits) {
+        const int tps = (tiles + splits - 1) / splits;
+        const int eff_splits = (tiles + tps - 1) / tps;
+        if (eff_splits != splits) continue;
+        const long wgs = (long)batch * hkv * groups * splits;
+        const long rounds = (wgs + kComputeUnits - 1) / kComputeUnits;
+        const double t_mfma = rounds * tps * simd * kTileBlockUs;
+        const double t_l2 = groups * kv_bytes / kL2BytesPerUs;
+        const double t_hbm = kv_bytes / kHbmBytesPerUs;
+        double t = std::max(t_mfma, std::max(t_l2, t_hbm)) + rounds * kFillUs;
+        if (splits > 1)
+          t += (double)batch * n_max * hq * splits * (head_dim + 2) * 4.0 * 2.0 /
+                   kCombineBytesPerUs + kFillUs;
+        if (t < best) {
+          best = t;
+          pl.n_row_groups = groups;
+          pl.rows_per_group = 16 * bpg;
+          pl.tiles_per_split = tps;
+          pl.n_splits = splits;
+        }
+      }
+    }
   } else {
     pl.n_row_groups = 1;
     pl.rows_per_group = (rows + 3) / 4 * 4;
-    per_seq_groups = pl.rows_per_group / 4;
+    const long base = (long)batch * hkv * (pl.rows_per_group / 4);
+    int splits = (int)max(1L, min((long)tiles, (512 + base - 1) / max(1L, base)));
+    splits = min(min(splits, max(1, tiles / 4)), kMaxSplits);
+    pl.tiles_per_split = (tiles + splits - 1) / splits;
+    pl.n_splits = (tiles + pl.tiles_per_split - 1) / pl.tiles_per_split;
   }
-  const long target = 512;  // workgroups to aim for (256 CUs x 2)
-  const long base = (long)batch * hkv * per_seq_groups;
-  int splits = (int)max(1L, min((long)tiles, (target + base - 1) / max(1L, base)));
-  // keep splits at least 4 tiles long so partial traffic stays small
-  splits = min(splits, max(1, tiles / 4));
-  splits = min(splits, kMaxSplits);
-  pl.tiles_per_split = (tiles + splits - 1) / splits;
-  if (pl.mfma && pl.tiles_per_split * 4 > kMaxSplitPages) pl.tiles_per_split = kMaxSplitPages / 4;
-  pl.n_splits = (tiles + pl.tiles_per_split - 1) / pl.tiles_per_split;
   const size_t prows = (size_t)batch * hkv * pl.n_row_groups * pl.n_splits * pl.rows_per_group;
   pl.part_o_bytes = pl.n_splits > 1 ? prows * head_dim * sizeof(float) : 0;
   pl.part_ml_bytes = pl.n_splits > 1 ? prows * 2 * sizeof(float) : 0;
@@ -716,7 +815,8 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
 }
 
 void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream) {
-  dim3 grid(p.n_splits, p.hkv * p.n_row_groups, p.batch);
+  const long clusters = (long)p.batch * p.hkv * p.n_splits;
+  dim3 grid((unsigned)(8 * p.n_row_groups * ((clusters + 7) / 8)));
   const int nb = (p.rows_per_group / 16 + kMfmaWaves - 1) / kMfmaWaves;
   switch (nb) {
     case 1: hipLaunchKernelGGL(attn_mfma_kernel<1>, grid, dim3(kMfmaThreads), 0, stream, p); break;
@@ -741,11 +841,12 @@ void launch_attention_wave(graft_dtype dtype, const AttnParams &p, hipStream_t s
 }
 
 void launch_attention_combine(graft_dtype dtype, const AttnParams &p, hipStream_t stream) {
-  dim3 grid(p.hq, p.n_max, p.batch);
+  const long rows = (long)p.batch * p.n_max * p.hq;
+  dim3 grid((unsigned)((rows + 3) / 4));
   if (dtype == GRAFT_F32)
-    hipLaunchKernelGGL(attn_combine_kernel<float>, grid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(attn_combine_kernel<float>, grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<__hip_bfloat16>, grid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(attn_combine_kernel<__hip_bfloat16>, grid, dim3(256), 0, stream, p);
 }
 
 }  // namespace graft

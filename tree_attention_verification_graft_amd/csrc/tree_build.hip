@@ -1,7 +1,13 @@
 // Hybrid tree assembly: prune the draft tree, fill the released budget from
 // the successor table M starting at the root, merge, and emit ancestor masks
-// and position ids.  One workgroup per sequence; every step is a
-// workgroup-parallel pass over at most 256 draft nodes / 127 slots in LDS.
+// and position ids.  One workgroup per sequence.
+//
+// Retrieval only needs the root token (the three-point summary of "Draft
+// Less, Retrieve More" has it start from the root in parallel with
+// drafting), so every envelope slot is resolved speculatively from the start
+// of the kernel, one envelope level per phase; each level's M lookups are in
+// flight while the workgroup does one phase of the pruning work in LDS.  The
+// merge then takes the first kmax - n_kept slots.
 //
 // Method: "Draft Less, Retrieve More" (aitrends.kr summary), method paragraph
 // steps one to three and the architecture paragraph; readings as documented
@@ -29,25 +35,23 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
   const graft_tree_config &cfg = p.cfg;
 
   __shared__ int32_t s_parent[kThreads];
-  __shared__ int32_t s_jump[kThreads];
-  __shared__ int32_t s_cnt[kThreads];
   __shared__ float s_pm[kThreads];
+  __shared__ uint8_t s_flag[kThreads];  // candidate, then kept
   __shared__ int32_t s_newidx[kThreads];
-  __shared__ uint8_t s_kept[kThreads];
   __shared__ uint32_t s_cmax[GRAFT_MAX_STAGES];
   __shared__ int32_t s_cexist[GRAFT_MAX_STAGES];
   __shared__ int32_t s_slot_tok[GRAFT_MAX_NODES];
-  __shared__ int32_t s_slot_level[GRAFT_MAX_NODES];
   __shared__ uint8_t s_slot_valid[GRAFT_MAX_NODES];
   __shared__ int32_t s_slot_new[GRAFT_MAX_NODES];
   __shared__ int32_t s_out_tok[GRAFT_MAX_NODES];
   __shared__ int32_t s_out_par[GRAFT_MAX_NODES];
-  __shared__ int32_t s_stage, s_kdraft, s_nkept, s_nvalid, s_maxlevel;
+  __shared__ int32_t s_nkept, s_nvalid, s_maxlevel;
 
   const int n = min(max(p.n_draft[b], 0), p.n_draft_max);
   const size_t drow = (size_t)b * p.n_draft_max;
   const int root = p.root_token[b];
   const bool root_ok = root >= 0 && root < p.vocab;
+  const int env = cfg.env_len;
 
   int32_t my_parent = -1, my_token = 0;
   float my_conf = 0.f;
@@ -57,41 +61,68 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
     my_conf = p.draft_conf[drow + tid];
     if (my_parent >= tid) my_parent = -1;  // precondition guard: parent < child
   }
+  // envelope level of slot tid (root children are level 0)
+  int my_level = -1;
+  if (tid < env) {
+    my_level = 0;
+    for (int j = cfg.env_parent[tid]; j >= 0; j = cfg.env_parent[j]) ++my_level;
+  }
   s_parent[tid] = my_parent;
-  s_jump[tid] = my_parent;
-  s_cnt[tid] = 1;
   s_pm[tid] = my_conf;
   s_newidx[tid] = 0;
   if (tid < GRAFT_MAX_STAGES) {
     s_cmax[tid] = 0u;
     s_cexist[tid] = 0;
   }
+  if (tid < GRAFT_MAX_NODES) {
+    s_slot_valid[tid] = 0;
+    s_slot_tok[tid] = -1;
+  }
   if (tid == 0) s_maxlevel = 0;
   __syncthreads();
+  if (tid < env) atomicMax(&s_maxlevel, my_level);
 
-  // Draft depth (children of the root are depth 0) and the minimum confidence
-  // along the root path, by pointer jumping: after round r each node covers
-  // the 2^r nearest nodes of its chain.
-  for (int r = 0; r < 8; ++r) {
-    int j = s_jump[tid];
-    int cnt = s_cnt[tid];
-    float pm = s_pm[tid];
-    int nj = j;
-    if (j >= 0) {
-      cnt += s_cnt[j];
-      pm = fminf(pm, s_pm[j]);
-      nj = s_jump[j];
+  // One envelope level: slots of level lv look up their parent's row of M.
+  // The load is issued here and its value stored by `finish` after the
+  // caller's phase of pruning work, so the two overlap.
+  int pending_tok = -1;
+  bool pending = false;
+  auto issue_level = [&](int lv) {
+    pending = tid < env && my_level == lv;
+    if (pending) {
+      const int ps = cfg.env_parent[tid];
+      const bool pok = ps < 0 ? root_ok : (s_slot_valid[ps] != 0);
+      const int ptok = ps < 0 ? root : s_slot_tok[ps];
+      pending_tok = pok ? p.m_ids[(size_t)ptok * p.top_s + cfg.env_rank[tid]] : -1;
     }
-    __syncthreads();
-    s_jump[tid] = nj;
-    s_cnt[tid] = cnt;
-    s_pm[tid] = pm;
-    __syncthreads();
-  }
-  const int my_depth = s_cnt[tid] - 1;
-  const float my_pm = s_pm[tid];
+  };
+  auto finish_level = [&]() {
+    if (pending) {
+      const bool ok = pending_tok >= 0 && pending_tok < p.vocab;
+      s_slot_tok[tid] = pending_tok;
+      s_slot_valid[tid] = ok ? 1 : 0;
+    }
+  };
 
-  // Depth confidence c_d = max confidence at each checkpoint depth.
+  // ---- phase 1: level 0 lookups || draft depth and path-minimum confidence
+  issue_level(0);
+  int my_depth = 0;  // children of the root have draft depth 0
+  float my_pm = my_conf;
+  if (tid < n) {
+    // parents precede children, so the walk has at most tid steps
+    int j = my_parent;
+    for (int steps = 0; j >= 0 && steps < tid; ++steps) {
+      ++my_depth;
+      my_pm = fminf(my_pm, s_pm[j]);
+      j = s_parent[j];
+    }
+  }
+  finish_level();
+  __syncthreads();
+  const int max_level = s_maxlevel;
+
+  // ---- phase 2: level 1 || depth confidence c_d = max at each checkpoint
+  issue_level(1);
   if (tid < n) {
     for (int s = 0; s < cfg.n_stages; ++s) {
       if (my_depth == cfg.stage_depth[s]) {
@@ -100,98 +131,76 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
       }
     }
   }
+  finish_level();
   __syncthreads();
-  if (tid == 0) {
-    int stage = -1;
-    for (int s = 0; s < cfg.n_stages; ++s) {
-      if (s_cexist[s] && key_float(s_cmax[s]) < cfg.stage_tau[s]) {
-        stage = s;
-        break;
-      }
+  // every thread takes the (uniform) stage decision from LDS
+  int stage = -1;
+  for (int s = 0; s < cfg.n_stages; ++s) {
+    if (s_cexist[s] && key_float(s_cmax[s]) < cfg.stage_tau[s]) {
+      stage = s;
+      break;
     }
-    s_stage = stage;
-    s_kdraft = cfg.kmax - (stage < 0 ? cfg.k_ret_none : cfg.stage_k_ret[stage]);
   }
-  __syncthreads();
-  const int stage = s_stage;
-  const int k_draft = s_kdraft;
-
-  // Candidates: every draft if nothing fires, else drafts no deeper than the
-  // firing checkpoint.  Keep the k_draft best by (path-min desc, index asc).
-  s_pm[tid] = my_pm;
+  const int k_draft = cfg.kmax - (stage < 0 ? cfg.k_ret_none : cfg.stage_k_ret[stage]);
   const bool cand = tid < n && (stage < 0 || my_depth <= cfg.stage_depth[stage]);
-  s_kept[tid] = cand ? 1 : 0;
+
+  // ---- phase 3: level 2 || candidates; keep the k_draft best by
+  // (path-min desc, index asc)
+  issue_level(2);
+  s_pm[tid] = my_pm;
+  s_flag[tid] = cand ? 1 : 0;
+  finish_level();
   __syncthreads();
+  issue_level(3);
   bool kept = false;
   if (cand) {
     int rank = 0;
     for (int j = 0; j < n; ++j) {
-      if (!s_kept[j] || j == tid) continue;
-      float pj = s_pm[j];
+      if (!s_flag[j] || j == tid) continue;
+      const float pj = s_pm[j];
       rank += (pj > my_pm) || (pj == my_pm && j < tid);
     }
     kept = rank < k_draft;
   }
+  finish_level();
   __syncthreads();
-  s_kept[tid] = kept ? 1 : 0;
+  s_flag[tid] = kept ? 1 : 0;
   __syncthreads();
 
-  // Compaction of kept drafts, in input order, after the root.
+  // ---- phase 4: level 4 || compaction of kept drafts after the root
+  issue_level(4);
   if (kept) {
     int before = 0;
-    for (int j = 0; j < tid; ++j) before += s_kept[j];
+    for (int j = 0; j < tid; ++j) before += s_flag[j];
     s_newidx[tid] = 1 + before;
   }
   if (tid == 0) {
-    int c = 0;
-    for (int j = 0; j < n; ++j) c += s_kept[j];
-    s_nkept = c;
+    int cnt = 0;
+    for (int j = 0; j < n; ++j) cnt += s_flag[j];
+    s_nkept = cnt;
   }
+  finish_level();
   __syncthreads();
+  // remaining envelope levels, if the envelope is deeper
+  for (int lv = 5; lv <= max_level; ++lv) {
+    issue_level(lv);
+    finish_level();
+    __syncthreads();
+  }
   const int n_kept = s_nkept;
   const int k_fill = cfg.kmax - n_kept;
 
-  // Retrieval: the first k_fill envelope slots, resolved level by level from
-  // the root downwards (a slot's token is a lookup in its parent's row).
-  int my_level = 0;
-  if (tid < k_fill) {
-    int j = cfg.env_parent[tid];
-    while (j >= 0) {
-      ++my_level;
-      j = cfg.env_parent[j];
-    }
-    s_slot_level[tid] = my_level;
-    s_slot_valid[tid] = 0;
-    s_slot_tok[tid] = -1;
-    atomicMax(&s_maxlevel, my_level);
-  }
-  __syncthreads();
-  const int max_level = s_maxlevel;
-  for (int lv = 0; lv <= max_level; ++lv) {
-    if (tid < k_fill && my_level == lv) {
-      const int ps = cfg.env_parent[tid];
-      const bool pok = ps < 0 ? root_ok : (s_slot_valid[ps] != 0);
-      const int ptok = ps < 0 ? root : s_slot_tok[ps];
-      int tok = -1;
-      bool ok = false;
-      if (pok) {
-        tok = p.m_ids[(size_t)ptok * p.top_s + cfg.env_rank[tid]];
-        ok = tok >= 0 && tok < p.vocab;
-      }
-      s_slot_tok[tid] = tok;
-      s_slot_valid[tid] = ok ? 1 : 0;
-    }
-    __syncthreads();
-  }
-  if (tid < k_fill && s_slot_valid[tid]) {
+  // valid slots among the first k_fill, compacted after the kept drafts
+  const bool slot_ok = tid < k_fill && s_slot_valid[tid];
+  if (slot_ok) {
     int before = 0;
     for (int j = 0; j < tid; ++j) before += s_slot_valid[j];
     s_slot_new[tid] = 1 + n_kept + before;
   }
   if (tid == 0) {
-    int c = 0;
-    for (int j = 0; j < k_fill; ++j) c += s_slot_valid[j];
-    s_nvalid = c;
+    int cnt = 0;
+    for (int j = 0; j < k_fill; ++j) cnt += s_slot_valid[j];
+    s_nvalid = cnt;
   }
   __syncthreads();
   const int n_nodes = 1 + n_kept + s_nvalid;
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
     s_out_tok[ni] = my_token;
     s_out_par[ni] = my_parent < 0 ? 0 : s_newidx[my_parent];
   }
-  if (tid < k_fill && s_slot_valid[tid]) {
+  if (slot_ok) {
     const int ni = s_slot_new[tid];
     const int ps = cfg.env_parent[tid];
     s_out_tok[ni] = s_slot_tok[tid];
