@@ -5,8 +5,8 @@
 // tree-attention path of the architecture paragraph of the "Draft Less,
 // Retrieve More" summary).
 //
-// Matrix-core path (bf16, head_dim 128): one workgroup of 4 waves owns a
-// (sequence, KV head, row group, prefix split).  The query rows of a KV head
+// Matrix-core path (bf16, head_dim 128): one workgroup of 8 waves (two per
+// SIMD) owns a (sequence, KV head, row group, prefix split).  The query rows of a KV head
 // are its tree nodes times the query heads of the group.  K and V tiles of 64
 // keys are staged from the paged cache into LDS once and shared by all waves;
 // each wave owns up to NB blocks of 16 query rows.  Scores are computed
