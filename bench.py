@@ -6,6 +6,16 @@ already resident in HBM.  Input sets rotate so that the live footprint
 exceeds the 256 MB Infinity Cache.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--gpus 1]
+
+Counter support (HBM traffic of the attention call, see profiles/):
+  --copy-calibration   after the timed steps, run a plain elementwise copy of
+                       256 MiB three times, so that a rocprofv3 --pmc pass over
+                       this process also measures what FETCH_SIZE/WRITE_SIZE
+                       report for a known number of bytes;
+  --traffic-from-pmc FETCH_DIR WRITE_DIR
+                       read two such passes (rocprofv3 --output-format csv) and
+                       record the attention call's HBM bytes per launch in
+                       profiles/attn_traffic.json (no GPU needed).
 """
 from __future__ import annotations
 
@@ -29,6 +39,8 @@ ROTATE_BYTES = 600 << 20          # rotate input sets beyond the 256 MB MALL
 ATTN_SRC = os.path.join(ROOT, "tree_attention_verification_graft_amd", "csrc",
                         "tree_attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+CALIBRATION_BYTES = 256 << 20     # size of the counter-calibration copy
+ATTN_KERNELS = ("attn_mfma_kernel", "attn_wave_kernel", "attn_combine_kernel")
 
 
 def log(msg):
@@ -62,6 +74,59 @@ def measured_traffic(name):
     if not e or e.get("kernel_source_sha") != kernel_source_sha():
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+def _pmc_means(run_dir, counter):
+    """Mean per-dispatch value of one counter, by kernel, from a rocprofv3
+    --output-format csv directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per_kernel = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in per_kernel.items()}
+
+
+def traffic_from_pmc(name, fetch_dir, write_dir):
+    """HBM bytes per attention call from FETCH_SIZE and WRITE_SIZE passes,
+    each scaled by what the same counter reads for the calibration copy
+    (CALIBRATION_BYTES read and written by one elementwise kernel)."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        means = _pmc_means(d, counter)
+        calib = [v for k, v in means.items() if "neg_kernel" in k or "NegFunctor" in k]
+        if not calib:
+            raise SystemExit(f"{counter}: no calibration copy kernel in {d}")
+        kib_calib = calib[0][0]
+        factor = kib_calib * 1024.0 / CALIBRATION_BYTES
+        call_kib = sum(v[0] for k, v in means.items() if any(a in k for a in ATTN_KERNELS))
+        out[counter] = {"calibration_kib": kib_calib, "factor": factor,
+                        "attention_call_kib": call_kib,
+                        "bytes_per_call": call_kib * 1024.0 / factor}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[name] = {
+        "kernel_source_sha": kernel_source_sha(),
+        "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_call"] +
+                                out["WRITE_SIZE"]["bytes_per_call"],
+        "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
+        "note": ("per graft_tree_attention call (attention kernel plus split combine); "
+                 "each counter divided by its reading per byte of a plain 256 MiB copy"),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(table[name], indent=1))
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -126,7 +191,12 @@ def main():
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-from-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.traffic_from_pmc:
+        traffic_from_pmc(args.config, *args.traffic_from_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -255,6 +325,14 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.copy_calibration:
+        src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copies done")
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (one thread)")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -98,8 +98,9 @@ def test_accept_and_update_validation():
     assert acc(wsb=8) == -3
     assert acc(b=0) == 0
     align = lambda x: -(-x // 256) * 256
-    # one packed (value, index) key per (row, 4096-wide vocab chunk)
-    assert lib.graft_accept_workspace_size(2, 65, 151936) == align(2 * 65 * 38 * 8)
+    # one packed (value, index) key per (row, vocab chunk); sized for the
+    # f32 chunk of 2048 entries, the smaller of the two dtypes' chunks
+    assert lib.graft_accept_workspace_size(2, 65, 151936) == align(2 * 65 * 75 * 8)
     upd = lambda **k: lib.graft_update_adjacency(FAKE, FAKE, k.get("v", 100), k.get("s", 8),
                                                  k.get("np", 4), k.get("st", 10), FAKE, FAKE,
                                                  k.get("ws", FAKE), k.get("wsb", 1 << 20),

@@ -1,8 +1,9 @@
 // Greedy (lossless) acceptance of the verified hybrid tree, in two launches.
 //
-// argmax_chunks_kernel streams the logits: every (node row, 4096-entry vocab
-// chunk) pair is one workgroup whose threads issue all of their 16-byte loads
-// before reducing, so a launch keeps the whole live logits tensor in flight.
+// argmax_chunks_kernel streams the logits: every (node row, 8 KB vocab
+// chunk) pair is one workgroup whose threads issue both of their 16-byte
+// loads before reducing, so a launch keeps the whole live logits tensor in
+// flight.
 // A chunk reduces to one packed 64-bit key whose high half is an
 // order-preserving image of the value (-0 folded onto +0) and whose low half
 // is the complemented index, so an unsigned max picks the largest value and,
@@ -24,7 +25,10 @@ namespace graft {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 4096;      // vocab entries per argmax workgroup
+constexpr int kLoads = 2;         // 16-byte loads per thread
+// vocab entries per argmax workgroup: 4096 bf16 or 2048 f32
+template <bool BF16>
+constexpr int chunk_len() { return kLoads * kThreads * (BF16 ? 8 : 4); }
 constexpr int kPathThreads = 256; // >= GRAFT_MAX_NODES
 
 __device__ inline uint32_t ord_bf16(uint32_t u) {
@@ -53,13 +57,13 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(AcceptParams p)
   const int b = row / p.n_max;
   const int i = row % p.n_max;
   if (i >= p.n_nodes[b]) return;  // rows past the tree are not read
+  constexpr int kChunk = chunk_len<BF16>();
   const int lo = c * kChunk;
   const int hi = min(p.vocab, lo + kChunk);
   unsigned long long best = 0ull;
   if (VEC) {
     // 16-byte loads; lo and hi are multiples of the vector width here
-    constexpr int kPer = BF16 ? 8 : 4;                 // values per load
-    constexpr int kLoads = kChunk / (kPer * kThreads);  // 2 (bf16) or 4 (f32)
+    constexpr int kPer = BF16 ? 8 : 4;  // values per load
     const uint4 *x = reinterpret_cast<const uint4 *>(
         static_cast<const char *>(p.logits) + (size_t)row * p.vocab * (BF16 ? 2 : 4));
     uint4 v[kLoads];
@@ -84,25 +88,25 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(AcceptParams p)
       }
     }
   } else {
-    constexpr int kLoads = kChunk / kThreads;  // 16 scalar loads per thread
-    uint32_t v[kLoads];
+    constexpr int kScalar = kChunk / kThreads;  // scalar loads per thread
+    uint32_t v[kScalar];
     if (BF16) {
       const uint16_t *x = static_cast<const uint16_t *>(p.logits) + (size_t)row * p.vocab;
 #pragma unroll
-      for (int k = 0; k < kLoads; ++k) {
+      for (int k = 0; k < kScalar; ++k) {
         const int e = lo + k * kThreads + threadIdx.x;
         v[k] = e < hi ? x[e] : 0u;
       }
     } else {
       const uint32_t *x = static_cast<const uint32_t *>(p.logits) + (size_t)row * p.vocab;
 #pragma unroll
-      for (int k = 0; k < kLoads; ++k) {
+      for (int k = 0; k < kScalar; ++k) {
         const int e = lo + k * kThreads + threadIdx.x;
         v[k] = e < hi ? x[e] : 0u;
       }
     }
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
+    for (int k = 0; k < kScalar; ++k) {
       const int e = lo + k * kThreads + threadIdx.x;
       if (e < hi) best = umax64(best, pack(BF16 ? ord_bf16(v[k]) : ord_f32(v[k]), e));
     }
@@ -222,7 +226,10 @@ __global__ __launch_bounds__(kPathThreads) void accept_path_kernel(AcceptParams 
 
 }  // namespace
 
-int32_t accept_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
+int32_t accept_chunks(graft_dtype dtype, int32_t vocab) {
+  const int len = dtype == GRAFT_BF16 ? chunk_len<true>() : chunk_len<false>();
+  return (vocab + len - 1) / len;
+}
 
 void launch_accept(graft_dtype dtype, const AcceptParams &p, hipStream_t stream) {
   dim3 g1(p.chunks, p.batch * p.n_max);

@@ -8,6 +8,8 @@
 
 #include "graft_internal.h"
 
+#include <algorithm>
+
 namespace graft {
 
 static thread_local char g_error[512] = "";
@@ -96,6 +98,13 @@ graft_status graft_build_tree(const graft_tree_config *cfg, int32_t batch,
   for (int j = cfg->env_len; j < GRAFT_MAX_NODES - 1; ++j) {
     p.cfg.env_parent[j] = -1;
     p.cfg.env_rank[j] = 0;
+  }
+  // envelope levels (parents precede their slots, checked above)
+  p.env_levels = 0;
+  for (int j = 0; j < GRAFT_MAX_NODES - 1; ++j) {
+    const int par = j < cfg->env_len ? cfg->env_parent[j] : -1;
+    p.env_level[j] = (int8_t)(j >= cfg->env_len ? -1 : par < 0 ? 0 : p.env_level[par] + 1);
+    if (j < cfg->env_len) p.env_levels = std::max(p.env_levels, p.env_level[j] + 1);
   }
   p.batch = batch;
   p.n_draft_max = n_draft_max;
@@ -222,8 +231,9 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
 // ------------------------------------------------------------------- accept
 size_t graft_accept_workspace_size(int32_t batch, int32_t n_max, int32_t vocab) {
   if (batch < 0 || n_max < 1 || n_max > GRAFT_MAX_NODES || vocab < 1) return 0;
-  return align_up((size_t)batch * n_max * accept_chunks(vocab) * sizeof(unsigned long long),
-                  256);
+  // sized for the larger of the two dtypes' chunk counts (f32)
+  return align_up(
+      (size_t)batch * n_max * accept_chunks(GRAFT_F32, vocab) * sizeof(unsigned long long), 256);
 }
 
 graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab,
@@ -252,7 +262,7 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32
   p.n_max = n_max;
   p.vocab = vocab;
   p.words = GRAFT_MASK_WORDS(n_max);
-  p.chunks = accept_chunks(vocab);
+  p.chunks = accept_chunks(dtype, vocab);
   p.logits = logits;
   p.tree_token = tree_token;
   p.tree_parent = tree_parent;

@@ -21,6 +21,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------- tree build
 struct BuildParams {
   graft_tree_config cfg;
+  int8_t env_level[GRAFT_MAX_NODES - 1];  // envelope depth of each slot (root children 0)
+  int32_t env_levels;                     // 1 + the deepest slot's level (0 if no slots)
   int32_t batch, n_draft_max, vocab, top_s, n_max, words;
   const int32_t *draft_parent;
   const int32_t *draft_token;
@@ -87,7 +89,7 @@ struct AcceptParams {
   int32_t *path_tokens;
   unsigned long long *partial;  // [batch * n_max][chunks] packed (value, ~index)
 };
-int32_t accept_chunks(int32_t vocab);
+int32_t accept_chunks(graft_dtype dtype, int32_t vocab);
 void launch_accept(graft_dtype dtype, const AcceptParams &p, hipStream_t stream);
 
 // ---------------------------------------------------------------- adjacency

@@ -159,6 +159,11 @@ struct MfmaCtx {
   int b, h, rg, split, tid, lane, n16, g4, wave;
   int n_nodes, P, G, rows_b, row0, n_pages_b, t_begin, n_pref, n_tree;
   uint32_t lds0;  // LDS byte address of stage 0
+  // The wave's page-table entries for the split's first three tiles and the
+  // sequence's first page, loaded before the prefix length is known (indices
+  // clamped to the table row; entries past the prefix are replaced later).
+  int pre_page[3];
+  int first_page;
 };
 
 // One wave's share, specialised on the number NA of 16-row query blocks it
@@ -168,6 +173,8 @@ template <int NA>
 __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
                                                uint8_t *smem) {
   constexpr int NQ = NA > 0 ? NA : 1;
+  // V operands read ahead of the softmax (all eight where registers allow)
+  constexpr int kVPre = NA >= 2 ? 4 : 8;
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
   const __bf16 *k_cache = static_cast<const __bf16 *>(p.k_cache);
   const __bf16 *v_cache = static_cast<const __bf16 *>(p.v_cache);
@@ -200,155 +207,173 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     l_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- asynchronous loads of prefix tile `it` (local index) into stage `st`
-  // from its four pages `pg`.
-  const size_t kv_head = (size_t)p.hkv;
-  // The page table is read-only for the whole kernel: reading it through the
-  // constant address space lets uniform indices become scalar loads.
+  // ---- asynchronous loads of the prefix tiles.  Every wave loads one page
+  // of each tile: waves 0..3 the K rows of page (wave & 3), waves 4..7 the V
+  // dim rows of that page, as four 1 KB blocks, so a wave needs one page id
+  // and one base address per tile.  The page table is read-only for the
+  // whole kernel: reading it through the constant address space lets
+  // uniform indices become scalar loads.
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32 *table = (const_i32 *)(p.block_table + (size_t)c.b * p.max_blocks);
-  // Unconditional scalar loads at clamped (uniform) indices: a page past
-  // the prefix becomes the sequence's last page, whose keys get masked.
-  const int last_page = max(c.n_pages_b - 1, 0);
-  auto tile_pages = [&](int it) {
-    const int pg0 = (c.t_begin + it) * 4;
-    int4 r;
-    r.x = table[__builtin_amdgcn_readfirstlane(min(pg0, last_page))];
-    r.y = table[__builtin_amdgcn_readfirstlane(min(pg0 + 1, last_page))];
-    r.z = table[__builtin_amdgcn_readfirstlane(min(pg0 + 2, last_page))];
-    r.w = table[__builtin_amdgcn_readfirstlane(min(pg0 + 3, last_page))];
-    return r;
+  const int my_page = wave & 3;
+  const bool my_v = wave >= 4;
+  const char *kv_base = reinterpret_cast<const char *>(my_v ? v_cache : k_cache) +
+                        (size_t)c.h * (kBlock * kD * 2);
+  const uint32_t page_stride = (uint32_t)p.hkv * (kBlock * kD * 2);
+  // LDS destination of block q within a stage (wave-uniform)
+  auto dma_dst = [&](int q) {
+    return my_v ? (uint32_t)(kKBytes + (4 * my_page + q) * 1024)
+                : (uint32_t)((8 * (my_page >> 1) + 2 * (my_page & 1) + (q & 1) + 4 * (q >> 1)) *
+                             1024);
   };
-  auto page_of = [](const int4 &pg, int i) {
-    return i == 0 ? pg.x : i == 1 ? pg.y : i == 2 ? pg.z : pg.w;
-  };
-  auto issue_prefix = [&](int st, const int4 &pg) {
-    const uint32_t sk = c.lds0 + st * kStageBytes;
-    const uint32_t sv = sk + kKBytes;
+  uint32_t dma_off[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int inst = wave + kMfmaWaves * r;  // 0..15, one 1 KB block each
-      // K: rows 4*inst .. +3 hold four keys of one page; lane -> row
-      // 4*inst + lane/16, chunk position lane%16
-      {
-        const int R = 4 * inst + (lane >> 4);
-        const int kl = key_of_krow(R);
-        const int blk =
-            __builtin_amdgcn_readfirstlane(page_of(pg, key_of_krow(4 * inst) >> 4));
-        const __bf16 *base = k_cache + ((size_t)blk * kv_head + c.h) * (kBlock * kD);
-        const uint32_t off = (uint32_t)((kl & 15) * 256 + (((lane & 15) ^ (R & 15)) << 4));
-        dma16(base, off, sk + inst * 1024);
-      }
-      // V: page inst/4, dim rows 32*(inst%4) .. +31; lane -> dim row
-      // 32*(inst%4) + lane/2, half position lane%2
-      {
-        const int blk = __builtin_amdgcn_readfirstlane(page_of(pg, inst >> 2));
-        const __bf16 *base = v_cache + ((size_t)blk * kv_head + c.h) * (kD * kBlock);
-        const int d = 32 * (inst & 3) + (lane >> 1);
-        const uint32_t off =
-            (uint32_t)(d * 32 + (((lane & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4));
-        dma16(base, off, sv + inst * 1024);
-      }
+  for (int q = 0; q < 4; ++q) {
+    if (!my_v) {
+      // K blocks of page j: inst = 8 (j >> 1) + 2 (j & 1) + {0, 1, 4, 5};
+      // block inst holds tile rows 4 inst .. + 3 (lane -> row 4 inst +
+      // lane / 16, chunk position lane % 16)
+      const int inst = 8 * (my_page >> 1) + 2 * (my_page & 1) + (q & 1) + 4 * (q >> 1);
+      const int R = 4 * inst + (lane >> 4);
+      const int kl = key_of_krow(R);
+      dma_off[q] = (uint32_t)((kl & 15) * 256 + (((lane & 15) ^ (R & 15)) << 4));
+    } else {
+      // V blocks of page j: dim rows 32 q .. + 31 (lane -> dim row 32 q +
+      // lane / 2, half position lane % 2)
+      const int d = 32 * q + (lane >> 1);
+      dma_off[q] = (uint32_t)(d * 32 + (((lane & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4));
     }
+  }
+  // The first three tiles' page ids were loaded before the prefix length
+  // was known, at indices clamped to the table row: a page past the prefix
+  // becomes the sequence's first page, whose keys there get masked (and its
+  // values zeroed).
+  auto fix_page = [&](int r, int it) {
+    return (c.t_begin + it) * 4 + my_page < c.n_pages_b ? r : c.first_page;
+  };
+  // In the loop the prefix length is known, so the index is clamped to the
+  // sequence's last page instead: the loaded id is used as it is, a tile
+  // later, and the scalar load never stalls the tile that issues it.
+  const int last_page = max(c.n_pages_b - 1, 0);
+  auto tile_page = [&](int it) {
+    return table[(uint32_t)min((c.t_begin + it) * 4 + my_page, last_page)];
+  };
+  auto issue_prefix = [&](int st, int blk) {
+    const char *base = kv_base + (uint64_t)(uint32_t)blk * page_stride;
+    const uint32_t sbase = c.lds0 + st * kStageBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(base, dma_off[q], sbase + dma_dst(q));
   };
 
-  // ---- one tile: two halves of 32 keys, each scores -> softmax -> P V.
-  // Half kp covers score blocks 2kp (keys 32kp + 8g + i) and 2kp+1
+  // ancestor masks of the wave's rows (read before the tree tiles)
+  uint32_t tmask[NQ][4];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) tmask[k][0] = tmask[k][1] = tmask[k][2] = tmask[k][3] = 0u;
+
+  // ---- one half tile (32 keys) in two pieces: scores, then softmax and
+  // P V.  Half kp covers score blocks 2kp (keys 32kp + 8g + i) and 2kp+1
   // (keys 32kp + 8g + 4 + i) of lane group g, which are exactly the eight
   // key slots lane group g feeds to the P V matrix op.
-  auto compute = [&](int st, int key0, bool tree) {
-    const uint8_t *sK = smem + st * kStageBytes;
-    const uint8_t *sV = sK + kKBytes;
-    const int limit = tree ? c.n_nodes : c.P;
-    const bool masked = tree || key0 + kTile > c.P;  // wave-uniform
-#pragma unroll 1
-    for (int kp = 0; kp < 2; ++kp) {
-      f32x4 s[NQ][2];
+  // Per-lane LDS offsets: K chunk kk of score-block row n16, and the V row
+  // of dim 16 d + n16 (its half-swap bit does not depend on d).
+  uint32_t k_off[4];
 #pragma unroll
-      for (int k = 0; k < NA; ++k) s[k][0] = s[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < 4; ++kk) k_off[kk] = n16 * 256 + (((4 * kk + g4) ^ n16) << 4);
+  const uint32_t v_off = (g4 >> 1) * 4096 + n16 * 32 +
+                         ((((g4 & 1) ^ (((n16 >> 2) ^ (n16 >> 3)) & 1))) << 4);
+  auto qk_half = [&](int st, int kp, f32x4 (&sc)[NQ][2]) {
+    const uint8_t *sK = smem + st * kStageBytes + kp * 8192;
+    // K operands are read two chunks (four operands) at a time ahead of
+    // their matrix ops (all eight at once for single-block waves)
+    constexpr int kKB = NA >= 2 ? 2 : 4;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 a[2];
+    for (int k = 0; k < NA; ++k) sc[k][0] = sc[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int R = 16 * (2 * kp + hh) + n16;
-          a[hh] = *reinterpret_cast<const bf16x8 *>(
-              sK + R * 256 + (((4 * kk + g4) ^ n16) << 4));
-        }
+    for (int kb = 0; kb < 4; kb += kKB) {
+      bf16x8 ka[kKB][2];
+#pragma unroll
+      for (int kk = 0; kk < kKB; ++kk)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          ka[kk][hh] = *reinterpret_cast<const bf16x8 *>(sK + hh * 4096 + k_off[kb + kk]);
+#pragma unroll
+      for (int kk = 0; kk < kKB; ++kk)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int k = 0; k < NA; ++k)
-            s[k][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[hh], qf[k][kk], s[k][hh],
-                                                               0, 0, 0);
-      }
-      bf16x8 pb[NQ];
+            sc[k][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk][hh], qf[k][kb + kk],
+                                                                sc[k][hh], 0, 0, 0);
+    }
+  };
+  auto sm_pv_half = [&](int st, int kp, int key0, bool tree, f32x4 (&sc)[NQ][2]) {
+    const uint8_t *sV = smem + st * kStageBytes + kKBytes + kp * 8192 + v_off;
+    // the first kVPre V operands are read before the softmax
+    bf16x8 va[kVPre];
 #pragma unroll
-      for (int k = 0; k < NA; ++k) {
-        if (masked) {
-          uint32_t mw[4] = {0u, 0u, 0u, 0u};
-          if (tree) {
-            const int r = row_of(k);
-            const int node = r < c.rows_b ? r / c.G : 0;
-            load_mask4(mw, p.tree_mask + ((size_t)c.b * p.n_max + node) * p.words, p.words);
-          }
+    for (int d = 0; d < kVPre; ++d) va[d] = *reinterpret_cast<const bf16x8 *>(sV + d * 512);
+    const int limit = tree ? c.n_nodes : c.P;
+    const bool masked = tree || key0 + kTile > c.P;  // wave-uniform
+    bf16x8 pb[NQ];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = key0 + 32 * kp + 8 * g4 + 4 * hh + i;
-              bool vis = key < limit;
-              if (tree) vis = vis && ((mask_word(mw, key >> 5) >> (key & 31)) & 1u);
-              s[k][hh][i] = vis ? s[k][hh][i] : -INFINITY;
-            }
-        }
-        // raw-score maximum of this half, then in log2 units
-        const float mx = group4_max(fmaxf(
-            fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3])),
-            fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3]))));
-        const float mxs = mx * p.scale_log2;
-        if (__ballot(mxs > m_run[k] + kRescaleLog2)) {
-          const float m_new = fmaxf(m_run[k], mxs);
-          const float alpha = fast_exp2(m_run[k] - m_new);
-          m_run[k] = m_new;
-          l_acc[k] *= alpha;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) o[k][d] *= alpha;
-        }
-        const float neg_m = -m_run[k];
-        bf16x8 v;
+    for (int k = 0; k < NA; ++k) {
+      f32x4(&s)[2] = sc[k];
+      if (masked) {
+        const uint32_t(&mw)[4] = tmask[k];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            v[4 * hh + i] = (__bf16)fast_exp2(fmaf(s[k][hh][i], p.scale_log2, neg_m));
-        pb[k] = v;
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 32 * kp + 8 * g4 + 4 * hh + i;
+            bool vis = key < limit;
+            if (tree) vis = vis && ((mask_word(mw, key >> 5) >> (key & 31)) & 1u);
+            s[hh][i] = vis ? s[hh][i] : -INFINITY;
+          }
       }
-      if (NA > 0) {
-        bf16x8 ones;
+      // raw-score maximum of this half, then in log2 units
+      const float mx = group4_max(fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                        fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))));
+      const float mxs = mx * p.scale_log2;
+      if (__ballot(mxs > m_run[k] + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run[k], mxs);
+        const float alpha = fast_exp2(m_run[k] - m_new);
+        m_run[k] = m_new;
+        l_acc[k] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
+        for (int d = 0; d < 8; ++d) o[k][d] *= alpha;
+      }
+      const float neg_m = -m_run[k];
+      bf16x8 v;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[4 * hh + i] = (__bf16)fast_exp2(fmaf(s[hh][i], p.scale_log2, neg_m));
+      pb[k] = v;
+    }
+    if (NA > 0) {
+      bf16x8 ones;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
+#pragma unroll
+      for (int k = 0; k < NA; ++k)
+        l_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], l_acc[k], 0, 0, 0);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const bf16x8 av = d < kVPre ? va[d < kVPre ? d : 0]
+                                    : *reinterpret_cast<const bf16x8 *>(sV + d * 512);
 #pragma unroll
         for (int k = 0; k < NA; ++k)
-          l_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], l_acc[k], 0, 0, 0);
-#pragma unroll
-        for (int d0 = 0; d0 < 8; d0 += 2) {
-          bf16x8 av[2];
-#pragma unroll
-          for (int dd = 0; dd < 2; ++dd) {
-            const int d = 16 * (d0 + dd) + n16;
-            av[dd] = *reinterpret_cast<const bf16x8 *>(
-                sV + (2 * kp + (g4 >> 1)) * 4096 + d * 32 +
-                (((g4 & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4));
-          }
-#pragma unroll
-          for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-            for (int k = 0; k < NA; ++k)
-              o[k][d0 + dd] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[dd], pb[k], o[k][d0 + dd], 0, 0, 0);
-        }
+          o[k][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[k], o[k][d], 0, 0, 0);
       }
+    }
+  };
+  auto compute = [&](int st, int key0, bool tree) {
+#pragma unroll 1
+    for (int kp = 0; kp < 2; ++kp) {
+      f32x4 sc[NQ][2];
+      qk_half(st, kp, sc);
+      sm_pv_half(st, kp, key0, tree, sc);
     }
   };
 
@@ -357,13 +382,18 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   // visible to the compiler (otherwise it would drain every load in flight
   // before the first matrix op of each tile); later stages are issued one
   // tile ahead of use with page ids fetched by scalar loads a tile earlier.
-  int4 pages_next = make_int4(0, 0, 0, 0);
-  if (c.n_pref > 0) issue_prefix(0, tile_pages(0));
-  if (c.n_pref > 1) issue_prefix(1, tile_pages(1));
-  if (c.n_pref > 2) pages_next = tile_pages(2);
+  // ---- prefix tiles through the stage ring.  Prologue: the first two
+  // stages are issued behind the query loads and the wait for both is made
+  // visible to the compiler (otherwise it would drain every load in flight
+  // before the first matrix op of each tile); later stages are issued three
+  // tiles ahead of use with page ids fetched by scalar loads a tile earlier.
+  int page_next = 0;
+  if (c.n_pref > 0) issue_prefix(0, fix_page(c.pre_page[0], 0));
+  if (c.n_pref > 1) issue_prefix(1, fix_page(c.pre_page[1], 1));
+  if (c.n_pref > 2) page_next = fix_page(c.pre_page[2], 2);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries and stages 0, 1
-  if (c.n_pref > 2) issue_prefix(2, pages_next);
-  if (c.n_pref > 3) pages_next = tile_pages(3);
+  if (c.n_pref > 2) issue_prefix(2, page_next);
+  if (c.n_pref > 3) page_next = tile_page(3);
   for (int it = 0; it < c.n_pref; ++it) {
     // stage `it` has landed once at most the loads issued after it remain
     const int after = min(c.n_pref - 1 - it, kStages - 2);
@@ -372,8 +402,8 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     else wait_vmcnt<0>();
     lds_barrier();  // every wave's loads for stage `it` are in LDS; stage it-1 is free
     if (it + kStages - 1 < c.n_pref) {
-      issue_prefix((it + kStages - 1) % kStages, pages_next);
-      if (it + kStages < c.n_pref) pages_next = tile_pages(it + kStages);
+      issue_prefix((it + kStages - 1) % kStages, page_next);
+      if (it + kStages < c.n_pref) page_next = tile_page(it + kStages);
     }
     const int st = it % kStages;
     const int key0 = (c.t_begin + it) * kTile;
@@ -394,6 +424,14 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   // ---- tree tiles (split 0 only): the keys are the tree nodes themselves.
   const __bf16 *k_tree = static_cast<const __bf16 *>(p.k_tree);
   const __bf16 *v_tree = static_cast<const __bf16 *>(p.v_tree);
+  if (c.n_tree > 0) {
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
+      const int r = row_of(k);
+      const int node = r < c.rows_b ? r / c.G : 0;
+      load_mask4(tmask[k], p.tree_mask + ((size_t)c.b * p.n_max + node) * p.words, p.words);
+    }
+  }
   for (int tt = 0; tt < c.n_tree; ++tt) {
     const int key0 = tt * kTile;
     uint8_t *sK = smem;  // stage 0 (all prefix loads have completed)
@@ -405,19 +443,44 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       const int ch = tid + kMfmaThreads * r;
       const int kl = ch >> 4, dc = ch & 15;
       const int j = key0 + kl;
-      uint4 kv = zero4(), vv = zero4();
-      if (j < c.n_nodes) {
-        const size_t base = (((size_t)c.b * p.n_max + j) * p.hkv + c.h) * kD + dc * 8;
-        kv = *reinterpret_cast<const uint4 *>(k_tree + base);
-        vv = *reinterpret_cast<const uint4 *>(v_tree + base);
-      }
+      uint4 kv = zero4();
+      if (j < c.n_nodes)
+        kv = *reinterpret_cast<const uint4 *>(
+            k_tree + (((size_t)c.b * p.n_max + j) * p.hkv + c.h) * kD + dc * 8);
       const int R = k_row_of_key(kl);
       *reinterpret_cast<uint4 *>(sK + R * 256 + ((dc ^ (R & 15)) << 4)) = kv;
-      const __bf16 *ve = reinterpret_cast<const __bf16 *>(&vv);
+    }
+    // V: thread t < 128 takes the 8 x 8 block of keys 8 * kc .. + 7 and
+    // dims 8 * dc .. + 7, transposes it in registers and writes eight
+    // 16-byte dim rows.
+    if (tid < 128) {
+      const int dc = tid & 15, kc = tid >> 4;
+      uint32_t w[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = key0 + 8 * kc + i;
+        uint4 vv = zero4();
+        if (j < c.n_nodes)
+          vv = *reinterpret_cast<const uint4 *>(
+              v_tree + (((size_t)c.b * p.n_max + j) * p.hkv + c.h) * kD + dc * 8);
+        w[i][0] = vv.x;
+        w[i][1] = vv.y;
+        w[i][2] = vv.z;
+        w[i][3] = vv.w;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        const int q = e >> 1;
+        uint32_t o4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a = w[2 * m][q], b2 = w[2 * m + 1][q];
+          o4[m] = (e & 1) ? ((a >> 16) | (b2 & 0xffff0000u)) : ((a & 0xffffu) | (b2 << 16));
+        }
         const int d = dc * 8 + e;
-        *reinterpret_cast<__bf16 *>(sV + v_lds_offset(d, kl)) = ve[e];
+        *reinterpret_cast<uint4 *>(sV + (kc >> 1) * 4096 + d * 32 +
+                                   (((kc & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4)) =
+            make_uint4(o4[0], o4[1], o4[2], o4[3]);
       }
     }
     lds_barrier();
@@ -485,6 +548,15 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  {
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const_i32 *trow = (const_i32 *)(p.block_table + (size_t)c.b * p.max_blocks);
+    const int last = p.max_blocks - 1;
+    const int pg0 = c.split * p.tiles_per_split * 4 + (c.wave & 3);
+    c.first_page = trow[0];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) c.pre_page[i] = trow[(uint32_t)min(pg0 + 4 * i, last)];
+  }
   c.n16 = c.lane & 15;
   c.g4 = c.lane >> 4;
   c.lds0 = (uint32_t)(uintptr_t)smem;
@@ -684,41 +756,63 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const float *po = p.part_o + (base * stride + rl) * p.head_dim;
   const int dpl = p.head_dim / 64;  // 1 or 2 dims per lane
 
-  float M = kNegBig;
-  for (int s0 = 0; s0 < active; s0 += 64)
-    if (s0 + lane < active) M = fmaxf(M, ml[(s0 + lane) * stride * 2]);
-  M = wave_max(M);
+  const size_t sstride = stride * p.head_dim;  // floats between splits
+  auto load_o = [&](int j) {
+    const float *src = po + (size_t)j * sstride + dpl * lane;
+    return dpl == 2 ? *reinterpret_cast<const float2 *>(src) : make_float2(src[0], 0.f);
+  };
   float L = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int s0 = 0; s0 < active; s0 += 64) {
-    float w = 0.f;
-    if (s0 + lane < active) {
-      const float *e = ml + (s0 + lane) * stride * 2;
-      w = fast_exp2(e[0] - M);
-      L += w * e[1];
-    }
-    const int n = min(64, active - s0);
-    const size_t sstride = stride * p.head_dim;
-    const float *o0 = po + (size_t)s0 * sstride + dpl * lane;
-    int j = 0;
-    for (; j + 8 <= n; j += 8) {  // eight independent loads in flight
-      float2 v[8];
+  if (active <= 64) {
+    // Every load is issued before the reductions: the first eight splits'
+    // values, and lane s's (max, sum) of split s.
+    float2 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = dpl == 2 ? *reinterpret_cast<const float2 *>(o0 + (size_t)(j + u) * sstride)
-                        : make_float2(o0[(size_t)(j + u) * sstride], 0.f);
+    for (int u = 0; u < 8; ++u) v[u] = u < active ? load_o(u) : make_float2(0.f, 0.f);
+    float m_s = kNegBig, l_s = 0.f;
+    if (lane < active) {
+      m_s = ml[(size_t)lane * stride * 2];
+      l_s = ml[(size_t)lane * stride * 2 + 1];
+    }
+    const float M = wave_max(m_s);
+    const float w = lane < active ? fast_exp2(m_s - M) : 0.f;
+    L = w * l_s;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+      acc0 += wj * v[u].x;
+      acc1 += wj * v[u].y;
+    }
+    for (int j0 = 8; j0 < active; j0 += 8) {
+      float2 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = j0 + u < active ? load_o(j0 + u) : make_float2(0.f, 0.f);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
-        acc0 += wj * v[u].x;
-        acc1 += wj * v[u].y;
+        const float wj =
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(j0 + u, 63)));
+        acc0 += wj * x[u].x;
+        acc1 += wj * x[u].y;
       }
     }
-    for (; j < n; ++j) {
-      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-      const float2 v = dpl == 2 ? *reinterpret_cast<const float2 *>(o0 + (size_t)j * sstride)
-                                : make_float2(o0[(size_t)j * sstride], 0.f);
-      acc0 += wj * v.x;
-      acc1 += wj * v.y;
+  } else {
+    float M = kNegBig;
+    for (int s0 = 0; s0 < active; s0 += 64)
+      if (s0 + lane < active) M = fmaxf(M, ml[(size_t)(s0 + lane) * stride * 2]);
+    M = wave_max(M);
+    for (int s0 = 0; s0 < active; s0 += 64) {
+      float w = 0.f;
+      if (s0 + lane < active) {
+        const float *e = ml + (size_t)(s0 + lane) * stride * 2;
+        w = fast_exp2(e[0] - M);
+        L += w * e[1];
+      }
+      const int n = min(64, active - s0);
+      for (int j = 0; j < n; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        const float2 x = load_o(s0 + j);
+        acc0 += wj * x.x;
+        acc1 += wj * x.y;
+      }
     }
   }
   const float inv = 1.f / wave_sum(L);
@@ -737,18 +831,23 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 // Launch planning.  Query rows per KV head are n_max * group, in blocks of
 // 16.  The matrix-core path holds one workgroup per compute unit (its LDS
 // ring and registers fill one), so the plan picks the number of row groups
-// and prefix splits that minimise an estimate of
-//   rounds * tiles per workgroup * (blocks on the busiest SIMD)
-// plus a fill latency per round and, when the prefix is split, the split
-// partials' traffic through the combine.  The wavefront path splits the
-// prefix so the grid holds about two workgroups per compute unit.
+// and prefix splits that minimise an estimate of the kernel's time:
+//   rounds * tiles per workgroup * (a per-tile cost + a cost per 16-row
+//   block on the busiest SIMD)
+// bounded below by the HBM and L2 streams, plus a fixed cost per round
+// (dispatch, prologue, epilogue) and, when the prefix is split, the combine
+// launch and the split partials' traffic.  The constants are measured on
+// MI355X.  The wavefront path splits the prefix so the grid holds about two
+// workgroups per compute unit.
 namespace {
 constexpr int kComputeUnits = 256;
-constexpr double kTileBlockUs = 34.0 * 16.0 / 2400.0 / 0.45;  // one 16-row block, one tile
-constexpr double kFillUs = 3.0;
-constexpr double kCombineBytesPerUs = 4.0e6;  // partial traffic through the combine
+constexpr double kTileFixedUs = 0.6;          // per 64-key tile, any block count
+constexpr double kTileBlockUs = 0.4;          // per 16-row block on the busiest SIMD
+constexpr double kRoundUs = 6.0;              // dispatch + prologue + epilogue
+constexpr double kCombineUs = 4.0;            // combine launch
+constexpr double kPartialBytesPerUs = 5.0e6;  // partials written, then read back
 constexpr double kL2BytesPerUs = 16.0e6;      // KV re-reads by extra row groups (L2)
-constexpr double kHbmBytesPerUs = 6.0e6;      // streaming reads from HBM
+constexpr double kHbmBytesPerUs = 5.0e6;      // streaming reads from HBM
 
 int busiest_simd_blocks(int blocks_per_group) {
   int best = 0;
@@ -783,13 +882,13 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
         if (eff_splits != splits) continue;
         const long wgs = (long)batch * hkv * groups * splits;
         const long rounds = (wgs + kComputeUnits - 1) / kComputeUnits;
-        const double t_mfma = rounds * tps * simd * kTileBlockUs;
+        const double t_tiles = rounds * tps * (kTileFixedUs + simd * kTileBlockUs);
         const double t_l2 = groups * kv_bytes / kL2BytesPerUs;
         const double t_hbm = kv_bytes / kHbmBytesPerUs;
-        double t = std::max(t_mfma, std::max(t_l2, t_hbm)) + rounds * kFillUs;
+        double t = std::max(t_tiles, std::max(t_l2, t_hbm)) + rounds * kRoundUs;
         if (splits > 1)
-          t += (double)batch * n_max * hq * splits * (head_dim + 2) * 4.0 * 2.0 /
-                   kCombineBytesPerUs + kFillUs;
+          t += kCombineUs + (double)batch * n_max * hq * splits * (head_dim + 2) * 4.0 * 2.0 /
+                                kPartialBytesPerUs;
         if (t < best) {
           best = t;
           pl.n_row_groups = groups;

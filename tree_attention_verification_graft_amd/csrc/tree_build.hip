@@ -7,7 +7,11 @@
 // drafting), so every envelope slot is resolved speculatively from the start
 // of the kernel, one envelope level per phase; each level's M lookups are in
 // flight while the workgroup does one phase of the pruning work in LDS.  The
-// merge then takes the first kmax - n_kept slots.
+// merge then takes the first kmax - n_kept slots.  The chain of dependent
+// M lookups (one per envelope level) is the kernel's critical path, so every
+// other step is kept to a few LDS operations: counts and compactions are
+// wave ballots, and the best-K_draft selection only ranks when the
+// candidates exceed the budget.
 //
 // Method: "Draft Less, Retrieve More" (aitrends.kr summary), method paragraph
 // steps one to three and the architecture paragraph; readings as documented
@@ -18,6 +22,7 @@ namespace graft {
 namespace {
 
 constexpr int kThreads = 256;  // == GRAFT_MAX_DRAFT
+constexpr int kWaves = kThreads / 64;
 
 // Order-preserving map of a float onto uint32 (larger float -> larger uint).
 __device__ inline uint32_t float_key(float f) {
@@ -29,6 +34,29 @@ __device__ inline float key_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Block-wide exclusive count of `flag` over thread index, and the total.
+// `cnt` is a per-call LDS array of kWaves words; the call contains one
+// barrier.
+struct Count {
+  int before, total;
+};
+__device__ inline Count block_count(bool flag, uint32_t *cnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long bal = __ballot(flag);
+  if (lane == 0) cnt[wave] = (uint32_t)__popcll(bal);
+  __syncthreads();
+  Count r;
+  r.before = __popcll(bal & ((1ull << lane) - 1ull));
+  r.total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = (int)cnt[w];
+    r.before += w < wave ? c : 0;
+    r.total += c;
+  }
+  return r;
+}
+
 __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -36,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
 
   __shared__ int32_t s_parent[kThreads];
   __shared__ float s_pm[kThreads];
-  __shared__ uint8_t s_flag[kThreads];  // candidate, then kept
+  __shared__ unsigned long long s_key[kThreads];  // candidate keys, compacted
   __shared__ int32_t s_newidx[kThreads];
   __shared__ uint32_t s_cmax[GRAFT_MAX_STAGES];
   __shared__ int32_t s_cexist[GRAFT_MAX_STAGES];
@@ -45,31 +73,57 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
   __shared__ int32_t s_slot_new[GRAFT_MAX_NODES];
   __shared__ int32_t s_out_tok[GRAFT_MAX_NODES];
   __shared__ int32_t s_out_par[GRAFT_MAX_NODES];
-  __shared__ int32_t s_nkept, s_nvalid, s_maxlevel;
+  __shared__ uint32_t s_cnt[4][kWaves];
 
-  const int n = min(max(p.n_draft[b], 0), p.n_draft_max);
-  const size_t drow = (size_t)b * p.n_draft_max;
+  // ---- every input load is issued up front; none depends on another
+  const int n_raw = p.n_draft[b];
   const int root = p.root_token[b];
-  const bool root_ok = root >= 0 && root < p.vocab;
-  const int env = cfg.env_len;
-
+  const int prefix = p.prefix_len[b];
+  const size_t drow = (size_t)b * p.n_draft_max;
   int32_t my_parent = -1, my_token = 0;
   float my_conf = 0.f;
-  if (tid < n) {
+  if (tid < p.n_draft_max) {
     my_parent = p.draft_parent[drow + tid];
     my_token = p.draft_token[drow + tid];
     my_conf = p.draft_conf[drow + tid];
-    if (my_parent >= tid) my_parent = -1;  // precondition guard: parent < child
   }
-  // envelope level of slot tid (root children are level 0)
-  int my_level = -1;
+  const int env = cfg.env_len;
+  int env_par = -1, env_rank = 0, env_lvl = -1;
   if (tid < env) {
-    my_level = 0;
-    for (int j = cfg.env_parent[tid]; j >= 0; j = cfg.env_parent[j]) ++my_level;
+    env_par = cfg.env_parent[tid];
+    env_rank = cfg.env_rank[tid];
+    env_lvl = p.env_level[tid];
   }
+  const int n = min(max(n_raw, 0), p.n_draft_max);
+  const bool is_draft = tid < n;
+  if (!is_draft || my_parent >= tid) my_parent = -1;  // precondition guard: parent < child
+  const bool root_ok = root >= 0 && root < p.vocab;
+
+  // One envelope level: slots of level lv look up their parent's row of M.
+  // The load is issued by `issue_level` and its value stored by
+  // `finish_level` after the caller's phase of pruning work, so the two
+  // overlap.
+  int pending_tok = -1;
+  bool pending = false;
+  auto issue_level = [&](int lv) {
+    pending = tid < env && env_lvl == lv;
+    if (pending) {
+      const bool pok = env_par < 0 ? root_ok : (s_slot_valid[env_par] != 0);
+      const int ptok = env_par < 0 ? root : s_slot_tok[env_par];
+      pending_tok = pok ? p.m_ids[(size_t)ptok * p.top_s + env_rank] : -1;
+    }
+  };
+  auto finish_level = [&]() {
+    if (pending) {
+      s_slot_tok[tid] = pending_tok;
+      s_slot_valid[tid] = (pending_tok >= 0 && pending_tok < p.vocab) ? 1 : 0;
+    }
+  };
+
+  // ---- level 0 || draft depth and path-minimum confidence
+  issue_level(0);
   s_parent[tid] = my_parent;
   s_pm[tid] = my_conf;
-  s_newidx[tid] = 0;
   if (tid < GRAFT_MAX_STAGES) {
     s_cmax[tid] = 0u;
     s_cexist[tid] = 0;
@@ -78,37 +132,10 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
     s_slot_valid[tid] = 0;
     s_slot_tok[tid] = -1;
   }
-  if (tid == 0) s_maxlevel = 0;
   __syncthreads();
-  if (tid < env) atomicMax(&s_maxlevel, my_level);
-
-  // One envelope level: slots of level lv look up their parent's row of M.
-  // The load is issued here and its value stored by `finish` after the
-  // caller's phase of pruning work, so the two overlap.
-  int pending_tok = -1;
-  bool pending = false;
-  auto issue_level = [&](int lv) {
-    pending = tid < env && my_level == lv;
-    if (pending) {
-      const int ps = cfg.env_parent[tid];
-      const bool pok = ps < 0 ? root_ok : (s_slot_valid[ps] != 0);
-      const int ptok = ps < 0 ? root : s_slot_tok[ps];
-      pending_tok = pok ? p.m_ids[(size_t)ptok * p.top_s + cfg.env_rank[tid]] : -1;
-    }
-  };
-  auto finish_level = [&]() {
-    if (pending) {
-      const bool ok = pending_tok >= 0 && pending_tok < p.vocab;
-      s_slot_tok[tid] = pending_tok;
-      s_slot_valid[tid] = ok ? 1 : 0;
-    }
-  };
-
-  // ---- phase 1: level 0 lookups || draft depth and path-minimum confidence
-  issue_level(0);
   int my_depth = 0;  // children of the root have draft depth 0
   float my_pm = my_conf;
-  if (tid < n) {
+  if (is_draft) {
     // parents precede children, so the walk has at most tid steps
     int j = my_parent;
     for (int steps = 0; j >= 0 && steps < tid; ++steps) {
@@ -117,13 +144,8 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
       j = s_parent[j];
     }
   }
-  finish_level();
-  __syncthreads();
-  const int max_level = s_maxlevel;
-
-  // ---- phase 2: level 1 || depth confidence c_d = max at each checkpoint
-  issue_level(1);
-  if (tid < n) {
+  // depth confidence c_d = max over the drafts at each checkpoint depth
+  if (is_draft) {
     for (int s = 0; s < cfg.n_stages; ++s) {
       if (my_depth == cfg.stage_depth[s]) {
         atomicMax(&s_cmax[s], float_key(my_conf));
@@ -133,7 +155,9 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
   }
   finish_level();
   __syncthreads();
-  // every thread takes the (uniform) stage decision from LDS
+
+  // ---- level 1 || stage decision (uniform) and the candidate count
+  issue_level(1);
   int stage = -1;
   for (int s = 0; s < cfg.n_stages; ++s) {
     if (s_cexist[s] && key_float(s_cmax[s]) < cfg.stage_tau[s]) {
@@ -142,68 +166,46 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
     }
   }
   const int k_draft = cfg.kmax - (stage < 0 ? cfg.k_ret_none : cfg.stage_k_ret[stage]);
-  const bool cand = tid < n && (stage < 0 || my_depth <= cfg.stage_depth[stage]);
-
-  // ---- phase 3: level 2 || candidates; keep the k_draft best by
-  // (path-min desc, index asc)
-  issue_level(2);
-  s_pm[tid] = my_pm;
-  s_flag[tid] = cand ? 1 : 0;
-  finish_level();
-  __syncthreads();
-  issue_level(3);
-  bool kept = false;
-  if (cand) {
-    int rank = 0;
-    for (int j = 0; j < n; ++j) {
-      if (!s_flag[j] || j == tid) continue;
-      const float pj = s_pm[j];
-      rank += (pj > my_pm) || (pj == my_pm && j < tid);
+  const bool cand = is_draft && (stage < 0 || my_depth <= cfg.stage_depth[stage]);
+  const Count cc = block_count(cand, s_cnt[0]);
+  bool kept = cand;
+  if (cc.total > k_draft) {
+    // keep the k_draft best by (path-min desc, index asc): a candidate's
+    // rank is the number of candidate keys above its own
+    const unsigned long long key =
+        ((unsigned long long)float_key(my_pm) << 32) | (uint32_t)(kThreads - 1 - tid);
+    if (cand) s_key[cc.before] = key;
+    __syncthreads();
+    if (cand) {
+      int rank = 0;
+      for (int j = 0; j < cc.total; ++j) rank += s_key[j] > key;
+      kept = rank < k_draft;
     }
-    kept = rank < k_draft;
   }
   finish_level();
-  __syncthreads();
-  s_flag[tid] = kept ? 1 : 0;
   __syncthreads();
 
-  // ---- phase 4: level 4 || compaction of kept drafts after the root
-  issue_level(4);
-  if (kept) {
-    int before = 0;
-    for (int j = 0; j < tid; ++j) before += s_flag[j];
-    s_newidx[tid] = 1 + before;
-  }
-  if (tid == 0) {
-    int cnt = 0;
-    for (int j = 0; j < n; ++j) cnt += s_flag[j];
-    s_nkept = cnt;
-  }
+  // ---- level 2 || compaction of the kept drafts after the root
+  issue_level(2);
+  const Count ck = block_count(kept, s_cnt[1]);
+  s_newidx[tid] = kept ? 1 + ck.before : 0;
+  const int n_kept = ck.total;
   finish_level();
   __syncthreads();
-  // remaining envelope levels, if the envelope is deeper
-  for (int lv = 5; lv <= max_level; ++lv) {
+  // remaining envelope levels
+  for (int lv = 3; lv < p.env_levels; ++lv) {
     issue_level(lv);
     finish_level();
     __syncthreads();
   }
-  const int n_kept = s_nkept;
-  const int k_fill = cfg.kmax - n_kept;
 
   // valid slots among the first k_fill, compacted after the kept drafts
-  const bool slot_ok = tid < k_fill && s_slot_valid[tid];
-  if (slot_ok) {
-    int before = 0;
-    for (int j = 0; j < tid; ++j) before += s_slot_valid[j];
-    s_slot_new[tid] = 1 + n_kept + before;
-  }
-  if (tid == 0) {
-    int cnt = 0;
-    for (int j = 0; j < k_fill; ++j) cnt += s_slot_valid[j];
-    s_nvalid = cnt;
-  }
+  const int k_fill = cfg.kmax - n_kept;
+  const bool slot_ok = tid < k_fill && tid < env && s_slot_valid[tid];
+  const Count cs = block_count(slot_ok, s_cnt[2]);
+  if (slot_ok) s_slot_new[tid] = 1 + n_kept + cs.before;
+  const int n_nodes = 1 + n_kept + cs.total;
   __syncthreads();
-  const int n_nodes = 1 + n_kept + s_nvalid;
 
   // Merge: root, kept drafts, valid retrieval slots.
   if (tid == 0) {
@@ -217,9 +219,8 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
   }
   if (slot_ok) {
     const int ni = s_slot_new[tid];
-    const int ps = cfg.env_parent[tid];
     s_out_tok[ni] = s_slot_tok[tid];
-    s_out_par[ni] = ps < 0 ? 0 : s_slot_new[ps];
+    s_out_par[ni] = env_par < 0 ? 0 : s_slot_new[env_par];
   }
   __syncthreads();
 
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(BuildParams p) {
       }
       p.tree_token[o] = s_out_tok[tid];
       p.tree_parent[o] = s_out_par[tid];
-      p.tree_pos[o] = p.prefix_len[b] + d;
+      p.tree_pos[o] = prefix + d;
     } else {
       p.tree_token[o] = -1;
       p.tree_parent[o] = -1;
