@@ -3,7 +3,11 @@
 A step is the whole hot path over one batch: graft_build_tree ->
 graft_tree_attention -> graft_accept -> graft_update_adjacency, on inputs
 already resident in HBM.  Input sets rotate so that the live footprint
-exceeds the 256 MB Infinity Cache.  Prints one JSON line.
+exceeds the 256 MB Infinity Cache.  Each set's step is captured once in a
+HIP graph and the timed region replays the graphs (the eager time, with the
+Python launch path in between, is reported as ms_per_step_eager).  Per-call
+durations come from HIP events around replays of a graph that runs the
+call on 16 consecutive input sets.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--gpus 1]
 
@@ -40,6 +44,7 @@ ATTN_SRC = os.path.join(ROOT, "tree_attention_verification_graft_amd", "csrc",
                         "tree_attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 CALIBRATION_BYTES = 256 << 20     # size of the counter-calibration copy
+CALLS_PER_GRAPH = 16              # calls per graph for the per-call timings
 ATTN_KERNELS = ("attn_mfma_kernel", "attn_wave_kernel", "attn_combine_kernel")
 
 
@@ -243,41 +248,62 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def run(k, timed):
-        s = sets[k % n_sets]
-        if not timed:
-            s.step()
-            return None
-        e = [ev() for _ in range(5)]
-        e[0].record(stream)
-        s.build()
-        e[1].record(stream)
-        s.attention()
-        e[2].record(stream)
-        s.accept()
-        e[3].record(stream)
-        s.update()
-        e[4].record(stream)
-        return e
-
     for k in range(args.warmup):
-        run(k, False)
+        sets[k % n_sets].step()
+    torch.cuda.synchronize()
+
+    # eager whole-step time (host launch overhead included), for reference
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        sets[k % n_sets].step()
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # HIP graphs: one of the whole step per input set (a decode loop replays
+    # one step at a time), and, for per-call timing, one graph per call that
+    # runs it on CALLS_PER_GRAPH consecutive input sets, so that the graph
+    # launch cost does not hide the kernels' own duration.
+    calls = ("build", "attention", "accept", "update")
+    step_graphs = []
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.step()
+        step_graphs.append(g)
+    call_graphs = {}
+    for c in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(CALLS_PER_GRAPH):
+                getattr(sets[k % n_sets], c)()
+        call_graphs[c] = g
+    for k in range(args.warmup):
+        step_graphs[k % n_sets].replay()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
 
-    # whole-step throughput: no events inside the timed region
+    # whole-step throughput: graph replays, no events inside the timed region
     t0 = time.perf_counter()
     for k in range(args.steps):
-        run(k, False)
+        step_graphs[k % n_sets].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # per-call durations with HIP events on the launch stream
-    evs = [run(k, True) for k in range(args.steps)]
-    torch.cuda.synchronize()
-    comp = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
-    comp_ms = comp.mean(axis=0)
+    # per-call durations: HIP events on the launch stream around replays of
+    # each call's multi-call graph
+    reps = max(1, args.steps // CALLS_PER_GRAPH)
+    comp = []
+    for c in calls:
+        call_graphs[c].replay()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            call_graphs[c].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        comp.append(e0.elapsed_time(e1) / (reps * CALLS_PER_GRAPH))
+    comp_ms = np.array(comp)
 
     n_nodes = np.stack([to_host(s.n_nodes) for s in sets])
     tokens = float(n_nodes.sum(axis=1).mean())
@@ -287,7 +313,7 @@ def main():
     achieved = (kv_bytes + qo_bytes) / t_attn_s / 1e9
     kv_gbps = kv_bytes / t_attn_s / 1e9
     traffic = measured_traffic(w.name)
-    log(f"step {ms_per_step * 1e3:.1f} us; build {comp_ms[0] * 1e3:.1f} attn "
+    log(f"step {ms_per_step * 1e3:.1f} us (eager {ms_eager * 1e3:.1f}); build {comp_ms[0] * 1e3:.1f} attn "
         f"{comp_ms[1] * 1e3:.1f} accept {comp_ms[2] * 1e3:.1f} update "
         f"{comp_ms[3] * 1e3:.1f} us; attention {achieved:.0f} GB/s")
 
@@ -299,6 +325,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_eager": ms_eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
