@@ -144,7 +144,8 @@ graft_status graft_build_tree(const graft_tree_config *cfg, int32_t batch,
  * For sequence b, query head hq (KV head hq / (hq_count / hkv)) and tree
  * node i < n_nodes[b], the visible keys are all prefix tokens
  * 0 .. prefix_len[b]-1 of b and the tree nodes j whose bit is set in
- * tree_mask[b][i]; out = softmax(scale * q.k) weighted sum of v.  q and the
+ * tree_mask[b][i]; out = softmax(scale * q.k) weighted sum of v, with a
+ * finite scale > 0 (1/sqrt(head_dim) for standard attention).  q and the
  * keys are expected already position-rotated.  Rows i >= n_nodes[b] of out
  * are left untouched.
  *

@@ -80,6 +80,8 @@ def test_attention_validation():
     assert _attn(n_max=129) == -1
     assert _attn(max_blocks=2) == -1                          # 2*16 < max_prefix
     assert _attn(scale=float("inf")) == -1
+    assert _attn(scale=0.0) == -1
+    assert _attn(scale=-0.1) == -1
     assert _attn(batch=0) == 0
     # a long prefix needs split partials: no workspace -> workspace error
     need = lib.graft_tree_attention_workspace_size(1, 1, 61, 32, 8, 128, 65536)

@@ -175,7 +175,8 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
               (long long)max_blocks_per_seq * block_size >= (long long)max_prefix,
           GRAFT_ERR_INVALID_ARG,
           "graft_tree_attention: max_blocks_per_seq * block_size < max_prefix");
-  REQUIRE(std::isfinite(scale), GRAFT_ERR_INVALID_ARG, "graft_tree_attention: scale not finite");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention: scale must be finite and > 0");
   if (batch == 0) return GRAFT_OK;
   REQUIRE(q && k_tree && v_tree && k_cache && v_cache && block_table && prefix_len &&
               tree_mask && n_nodes && out,

@@ -44,15 +44,32 @@ constexpr int kMaxNB = 3;          // 16-row blocks per wave
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of two finite-or-(-inf) floats as one v_med3_f32 (median of a, b
+// and +inf); unlike fmaxf it needs no NaN canonicalisation of its inputs.
+// The +inf operand goes through an empty asm statement so that the compiler
+// cannot turn the median back into maxnum.
+__device__ inline float pos_inf() {
+  float x = INFINITY;
+  asm volatile("" : "+s"(x));
+  return x;
+}
+__device__ inline float fmax2(float a, float b, float inf) {
+  return __builtin_amdgcn_fmed3f(a, b, inf);
+}
+__device__ inline float max8(const f32x4 &a, const f32x4 &b, float inf) {
+  return fmax2(fmax2(fmax2(a[0], a[1], inf), fmax2(a[2], a[3], inf), inf),
+               fmax2(fmax2(b[0], b[1], inf), fmax2(b[2], b[3], inf), inf), inf);
+}
+
 // Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
 // l^48) with the gfx950 row-swap permutes, which stay in the vector ALU.
-__device__ inline float group4_max(float x) {
+__device__ inline float group4_max(float x, float inf) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float m1 = fmax2(__uint_as_float(a[0]), __uint_as_float(a[1]), inf);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax2(__uint_as_float(b[0]), __uint_as_float(b[1]), inf);
 }
 __device__ inline float group4_sum(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -188,6 +205,11 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   // holds the sum over all keys of the lane's query.
   f32x4 l_acc[NQ];
   float m_run[NQ];
+  // raw score above which a block must move its exponent offset:
+  // (m_run + kRescaleLog2) / (scale * log2 e)
+  float thr_raw[NQ];
+  const float inv_scale_log2 = 1.f / p.scale_log2;
+  const float pinf = pos_inf();
   auto row_of = [&](int k) { return c.row0 + 16 * (wave + kMfmaWaves * k) + n16; };
 #pragma unroll
   for (int k = 0; k < NA; ++k) {
@@ -204,6 +226,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[k][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[k] = kNegBig;
+    thr_raw[k] = kNegBig;  // the first scores always set the offset
     l_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
@@ -318,7 +341,17 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
 #pragma unroll
     for (int k = 0; k < NA; ++k) {
       f32x4(&s)[2] = sc[k];
-      if (masked) {
+      bool rescale;
+      float mx;
+      if (!masked) {
+        // Common case: the lane's own maximum of its 8 raw scores against
+        // the raw-score threshold of the lazy rescale; the exact maximum
+        // over the half (across the four lane groups) is only needed when
+        // some score crosses it.
+        mx = max8(s[0], s[1], pinf);
+        rescale = __ballot(mx > thr_raw[k]) != 0ull;
+        if (rescale) mx = group4_max(mx, pinf);
+      } else {
         const uint32_t(&mw)[4] = tmask[k];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -329,15 +362,15 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
             if (tree) vis = vis && ((mask_word(mw, key >> 5) >> (key & 31)) & 1u);
             s[hh][i] = vis ? s[hh][i] : -INFINITY;
           }
+        mx = group4_max(max8(s[0], s[1], pinf), pinf);
+        rescale = __ballot(mx * p.scale_log2 > m_run[k] + kRescaleLog2) != 0ull;
       }
-      // raw-score maximum of this half, then in log2 units
-      const float mx = group4_max(fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                        fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))));
-      const float mxs = mx * p.scale_log2;
-      if (__ballot(mxs > m_run[k] + kRescaleLog2)) {
-        const float m_new = fmaxf(m_run[k], mxs);
+      if (rescale) {
+        // new offset: the half's maximum (in log2 units) if it is larger
+        const float m_new = fmaxf(m_run[k], mx * p.scale_log2);
         const float alpha = fast_exp2(m_run[k] - m_new);
         m_run[k] = m_new;
+        thr_raw[k] = (m_new + kRescaleLog2) * inv_scale_log2;
         l_acc[k] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) o[k][d] *= alpha;
