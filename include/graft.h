@@ -197,8 +197,8 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
  * Inputs: logits [batch][n_max][vocab] (dtype); tree arrays as produced by
  * graft_build_tree.
  * workspace: >= graft_accept_workspace_size(...) bytes, any contents (one
- * packed value/index key per node row and vocabulary chunk of 2048 f32 or
- * 4096 bf16 entries).
+ * packed value/index key per node row and vocabulary chunk; chunks hold
+ * 2048 to 16384 entries).
  * Calls that share one workspace must not overlap.
  */
 size_t graft_accept_workspace_size(int32_t batch, int32_t n_max, int32_t vocab);

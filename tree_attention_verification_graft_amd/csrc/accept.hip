@@ -1,9 +1,11 @@
 // Greedy (lossless) acceptance of the verified hybrid tree, in two launches.
 //
-// argmax_chunks_kernel streams the logits: every (node row, 8 KB vocab
-// chunk) pair is one workgroup whose threads issue both of their 16-byte
-// loads before reducing, so a launch keeps the whole live logits tensor in
-// flight.
+// argmax_chunks_kernel streams the logits: every (node row, vocab chunk)
+// pair is one workgroup whose threads issue all of their 16-byte loads
+// before reducing, so a launch keeps the whole live logits tensor in flight.
+// Chunks are 8 KB (two loads per thread) when the grid would otherwise be
+// small, and 32 KB (eight loads) for large batches, where fewer and larger
+// workgroups dispatch faster.
 // A chunk reduces to one packed 64-bit key whose high half is an
 // order-preserving image of the value (-0 folded onto +0) and whose low half
 // is the complemented index, so an unsigned max picks the largest value and,
@@ -25,10 +27,12 @@ namespace graft {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLoads = 2;         // 16-byte loads per thread
-// vocab entries per argmax workgroup: 4096 bf16 or 2048 f32
-template <bool BF16>
-constexpr int chunk_len() { return kLoads * kThreads * (BF16 ? 8 : 4); }
+constexpr int kSmallLoads = 2;      // 16-byte loads per thread, small grids
+constexpr int kLargeLoads = 8;      // ... large grids
+constexpr int kLargeGrid = 8192;    // workgroups above which chunks grow
+// vocab entries per argmax workgroup: L * 2048 bf16 or L * 1024 f32
+template <bool BF16, int L>
+constexpr int chunk_len() { return L * kThreads * (BF16 ? 8 : 4); }
 constexpr int kPathThreads = 256; // >= GRAFT_MAX_NODES
 
 __device__ inline uint32_t ord_bf16(uint32_t u) {
@@ -50,14 +54,14 @@ __device__ inline unsigned long long wave_max64(unsigned long long v) {
   return v;
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int kLoads>
 __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(AcceptParams p) {
   const int c = blockIdx.x;
   const int row = blockIdx.y;  // b * n_max + i
   const int b = row / p.n_max;
   const int i = row % p.n_max;
   if (i >= p.n_nodes[b]) return;  // rows past the tree are not read
-  constexpr int kChunk = chunk_len<BF16>();
+  constexpr int kChunk = chunk_len<BF16, kLoads>();
   const int lo = c * kChunk;
   const int hi = min(p.vocab, lo + kChunk);
   unsigned long long best = 0ull;
@@ -226,21 +230,42 @@ __global__ __launch_bounds__(kPathThreads) void accept_path_kernel(AcceptParams 
 
 }  // namespace
 
-int32_t accept_chunks(graft_dtype dtype, int32_t vocab) {
-  const int len = dtype == GRAFT_BF16 ? chunk_len<true>() : chunk_len<false>();
+static int chunk_of(graft_dtype dtype, int loads) {
+  return loads * kThreads * (dtype == GRAFT_BF16 ? 8 : 4);
+}
+static bool vec_ok(graft_dtype dtype, int32_t vocab) {
+  return dtype == GRAFT_BF16 ? vocab % 8 == 0 : vocab % 4 == 0;
+}
+// Loads per thread of a launch: the larger chunks only for 16-byte-aligned
+// rows whose small-chunk grid would exceed kLargeGrid workgroups.
+static int loads_for(graft_dtype dtype, int32_t rows, int32_t vocab) {
+  const long small = (long)rows * ((vocab + chunk_of(dtype, kSmallLoads) - 1) /
+                                   chunk_of(dtype, kSmallLoads));
+  return vec_ok(dtype, vocab) && small > kLargeGrid ? kLargeLoads : kSmallLoads;
+}
+
+int32_t accept_chunks(graft_dtype dtype, int32_t rows, int32_t vocab) {
+  const int len = chunk_of(dtype, loads_for(dtype, rows, vocab));
+  return (vocab + len - 1) / len;
+}
+int32_t accept_chunks_max(int32_t vocab) {
+  const int len = chunk_of(GRAFT_F32, kSmallLoads);  // the smallest chunk
   return (vocab + len - 1) / len;
 }
 
 void launch_accept(graft_dtype dtype, const AcceptParams &p, hipStream_t stream) {
   dim3 g1(p.chunks, p.batch * p.n_max);
   const bool bf = dtype == GRAFT_BF16;
-  const bool vec = bf ? (p.vocab % 8 == 0) : (p.vocab % 4 == 0);
+  const bool vec = vec_ok(dtype, p.vocab);
+  const bool large = loads_for(dtype, p.batch * p.n_max, p.vocab) == kLargeLoads;
   if (bf) {
-    if (vec) hipLaunchKernelGGL((argmax_chunks_kernel<true, true>), g1, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((argmax_chunks_kernel<true, false>), g1, dim3(kThreads), 0, stream, p);
+    if (large) hipLaunchKernelGGL((argmax_chunks_kernel<true, true, kLargeLoads>), g1, dim3(kThreads), 0, stream, p);
+    else if (vec) hipLaunchKernelGGL((argmax_chunks_kernel<true, true, kSmallLoads>), g1, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((argmax_chunks_kernel<true, false, kSmallLoads>), g1, dim3(kThreads), 0, stream, p);
   } else {
-    if (vec) hipLaunchKernelGGL((argmax_chunks_kernel<false, true>), g1, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((argmax_chunks_kernel<false, false>), g1, dim3(kThreads), 0, stream, p);
+    if (large) hipLaunchKernelGGL((argmax_chunks_kernel<false, true, kLargeLoads>), g1, dim3(kThreads), 0, stream, p);
+    else if (vec) hipLaunchKernelGGL((argmax_chunks_kernel<false, true, kSmallLoads>), g1, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((argmax_chunks_kernel<false, false, kSmallLoads>), g1, dim3(kThreads), 0, stream, p);
   }
   hipLaunchKernelGGL(accept_path_kernel, dim3(p.batch), dim3(kPathThreads), 0, stream, p);
 }

@@ -232,9 +232,9 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
 // ------------------------------------------------------------------- accept
 size_t graft_accept_workspace_size(int32_t batch, int32_t n_max, int32_t vocab) {
   if (batch < 0 || n_max < 1 || n_max > GRAFT_MAX_NODES || vocab < 1) return 0;
-  // sized for the larger of the two dtypes' chunk counts (f32)
+  // sized for the largest chunk count any launch uses
   return align_up(
-      (size_t)batch * n_max * accept_chunks(GRAFT_F32, vocab) * sizeof(unsigned long long), 256);
+      (size_t)batch * n_max * accept_chunks_max(vocab) * sizeof(unsigned long long), 256);
 }
 
 graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab,
@@ -263,7 +263,7 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32
   p.n_max = n_max;
   p.vocab = vocab;
   p.words = GRAFT_MASK_WORDS(n_max);
-  p.chunks = accept_chunks(dtype, vocab);
+  p.chunks = accept_chunks(dtype, batch * n_max, vocab);
   p.logits = logits;
   p.tree_token = tree_token;
   p.tree_parent = tree_parent;

@@ -89,7 +89,9 @@ struct AcceptParams {
   int32_t *path_tokens;
   unsigned long long *partial;  // [batch * n_max][chunks] packed (value, ~index)
 };
-int32_t accept_chunks(graft_dtype dtype, int32_t vocab);
+// Vocabulary chunks per row of one launch, and the most any launch uses.
+int32_t accept_chunks(graft_dtype dtype, int32_t rows, int32_t vocab);
+int32_t accept_chunks_max(int32_t vocab);
 void launch_accept(graft_dtype dtype, const AcceptParams &p, hipStream_t stream);
 
 // ---------------------------------------------------------------- adjacency
