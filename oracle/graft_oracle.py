@@ -28,6 +28,9 @@ paragraph is named by its content):
 Where the pages leave a step open, the reading taken is stated in the function
 that implements it; the full list of readings lives with the design notes.
 
+O5 (append_kv) commits the accepted path to the KV cache, the step that
+follows verification when decoding continues.
+
 Conventions shared with the C header (by specification, not by code):
   * draft arrays  [B][n_draft_max]: parent (-1 = child of the root; otherwise
     an earlier index), token, conf (float32);
@@ -412,3 +415,44 @@ def update_adjacency(m_ids, m_scores, path_tokens, accept_len):
             ids[u, s] = v
             scores[u, s] = np.float32(sc)
     return ids, scores
+
+
+# ----------------------------------------------------------------------------
+# O5: committing the accepted path to the KV cache  ([AT-arch] one target
+# forward verifies the tree and decoding continues from the accepted tokens)
+# ----------------------------------------------------------------------------
+
+def append_kv(k_cache, v_cache, block_table, prefix_len, k_tree, v_tree,
+              path_nodes, accept_len):
+    """Write the K/V of each sequence's accepted path into its paged cache.
+
+    Reading: the verified tokens that decoding keeps are the root and the
+    accepted nodes, path_nodes[b][0 .. accept_len[b]]; node path_nodes[b][j]
+    sits at tree depth j, so its K/V (computed in the verification pass at
+    position prefix_len + j) becomes cache token prefix_len + j.  The bonus
+    token is not part of the tree: its K/V comes from the next step, where it
+    is the root.  K pages are token-major [blocks][Hkv][block][D], V pages
+    dim-major [blocks][Hkv][D][block].
+
+    Returns new (k_cache, v_cache, prefix_len); inputs are not modified.
+    Raises ValueError if a sequence's pages cannot hold the new tokens."""
+    k = np.array(k_cache, copy=True)
+    v = np.array(v_cache, copy=True)
+    blk = k.shape[2]
+    B = len(prefix_len)
+    new_len = np.array(prefix_len, dtype=np.int32, copy=True)
+    for b in range(B):
+        L = int(accept_len[b])
+        P = int(prefix_len[b])
+        if L < 0:
+            continue
+        if P + L + 1 > len(block_table[b]) * blk:
+            raise ValueError("the page table cannot hold the accepted tokens")
+        for j in range(L + 1):
+            node = int(path_nodes[b][j])
+            t = P + j
+            page = int(block_table[b][t // blk])
+            k[page, :, t % blk, :] = k_tree[b, node, :, :]
+            v[page, :, :, t % blk] = v_tree[b, node, :, :]
+        new_len[b] = P + L + 1
+    return k, v, new_len

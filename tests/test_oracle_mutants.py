@@ -13,6 +13,7 @@ import pytest
 
 import oracle.graft_oracle as real
 import test_oracle_accept_update as T_au
+import test_oracle_append as T_ap
 import test_oracle_attention as T_at
 import test_oracle_build_tree as T_bt
 
@@ -40,6 +41,10 @@ MUTANTS = [
     ("update ties by id desc", "key=lambda kv: (-kv[1], kv[0]))[:S]", "key=lambda kv: (-kv[1], -kv[0]))[:S]"),
     ("update forgets old score", "cand[v] = cand.get(v, 0.0) + float(c)", "cand[v] = float(c)"),
     ("bonus transition dropped", "for k in range(L + 1):", "for k in range(L):"),
+    ("commit one slot late", "            t = P + j\n", "            t = P + j + 1\n"),
+    ("commit drops the deepest node", "        for j in range(L + 1):\n            node", "        for j in range(L):\n            node"),
+    ("commit length short", "new_len[b] = P + L + 1", "new_len[b] = P + L"),
+    ("commit V from K", "v[page, :, :, t % blk] = v_tree[b, node, :, :]", "v[page, :, :, t % blk] = k_tree[b, node, :, :]"),
 ]
 
 
@@ -78,13 +83,18 @@ def _pin_calls():
               T_au.test_prompt_seeding_is_exact_top_bigrams]
     for s in range(20):
         calls.append(lambda s=s: T_au.test_update_matches_brute_force_and_is_order_free(s))
+    for s in range(8):
+        calls.append(lambda s=s: T_ap.test_append_identity_layout(s))
+    for s in range(6):
+        calls.append(lambda s=s: T_ap.test_committed_cache_decodes_like_the_verified_row(s))
+    calls.append(T_ap.test_root_only_and_capacity)
     return calls
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(name, old, new, monkeypatch):
     mod = _mutant_module(old, new)
-    for t in (T_bt, T_at, T_au):
+    for t in (T_bt, T_at, T_au, T_ap):
         monkeypatch.setattr(t, "O", mod)
     failed = 0
     for call in _pin_calls():

@@ -266,8 +266,10 @@ def make_from_spec(name: str, spec: dict) -> Workload:
     if "prefix_list" in spec:
         prefix_len = np.asarray(spec["prefix_list"], np.int32)
 
-    # paged layout: each sequence owns ceil(P/block) pages (at least one)
-    pages_per_seq = [max(1, -(-int(p) // block)) for p in prefix_len]
+    # paged layout: each sequence owns the pages of its prefix plus room for
+    # the n_max tokens a step can commit after verification
+    reserve = int(spec.get("reserve", n_max))
+    pages_per_seq = [max(1, -(-(int(p) + reserve) // block)) for p in prefix_len]
     max_blocks = max(pages_per_seq) if B else 1
     num_blocks = int(sum(pages_per_seq))
     phys = np.arange(num_blocks, dtype=np.int32)
