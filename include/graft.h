@@ -13,6 +13,7 @@
  *   graft_tree_attention    verify the hybrid tree with tree-masked attention
  *   graft_accept            greedy (lossless) longest-path acceptance
  *   graft_update_adjacency  online update of the successor table M
+ *   graft_append_kv         commit of the accepted path to the KV cache
  *
  * Conventions for every call
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -242,6 +243,38 @@ graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t voc
                                     int32_t path_stride, const int32_t *path_tokens,
                                     const int32_t *accept_len, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * graft_append_kv -- commit the accepted path to the paged KV cache, the
+ * step after verification (architecture paragraph: one target forward
+ * verifies the hybrid tree and decoding continues from the accepted tokens).
+ *
+ * For sequence b with L = accept_len[b] >= 0: tree node path_nodes[b][j]
+ * (j = 0 .. L: the root, then the accepted nodes, as written by
+ * graft_accept) sits at tree depth j, so its K/V (computed in the
+ * verification pass at position prefix_len[b] + j) is written to cache
+ * token prefix_len[b] + j for every KV head.  new_prefix_len[b] =
+ * prefix_len[b] + L + 1, or prefix_len[b] when L < 0.  The bonus token is
+ * not in the tree: its K/V comes from the next step, where it is the root.
+ *
+ * Layouts as graft_tree_attention: k_tree, v_tree [batch][n_max][hkv]
+ * [head_dim]; k_cache [num_blocks][hkv][block_size][head_dim] (token-major
+ * pages), v_cache [num_blocks][hkv][head_dim][block_size] (dim-major);
+ * block_table int32 [batch][max_blocks_per_seq]; path_nodes int32
+ * [batch][n_max]; prefix_len, accept_len, new_prefix_len int32 [batch].
+ * Precondition: the table maps every position below prefix_len[b] + L + 1
+ * to a page in [0, num_blocks).  Positions past max_blocks_per_seq *
+ * block_size, pages outside [0, num_blocks) and path entries outside
+ * [0, n_max) are skipped (never written).  new_prefix_len must not alias
+ * prefix_len.  Only the committed slots of the caches are written.
+ */
+graft_status graft_append_kv(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hkv,
+                             int32_t head_dim, const void *k_tree, const void *v_tree,
+                             void *k_cache, void *v_cache, int32_t num_blocks,
+                             int32_t block_size, const int32_t *block_table,
+                             int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                             const int32_t *path_nodes, const int32_t *accept_len,
+                             int32_t *new_prefix_len, hipStream_t stream);
 
 /* Message for the last non-OK status returned on this thread. */
 const char *graft_last_error(void);

@@ -23,10 +23,10 @@ def header_functions():
     return sorted(set(re.findall(r"^\S.*?\b(graft_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     names = header_functions()
     for n in ["graft_build_tree", "graft_tree_attention", "graft_accept",
-              "graft_update_adjacency"]:
+              "graft_update_adjacency", "graft_append_kv"]:
         assert n in names
 
 
@@ -119,3 +119,19 @@ def test_accept_and_update_validation():
 
 def test_version_string():
     assert "gfx950" in G.graft_version()
+
+
+def test_append_kv_validation():
+    def app(**k):
+        return lib.graft_append_kv(k.get("dt", 1), k.get("b", 2), k.get("n", 9), k.get("hkv", 2),
+                                   k.get("d", 128), k.get("kt", FAKE), FAKE, FAKE, FAKE,
+                                   k.get("nblk", 64), k.get("blk", 16), FAKE, k.get("mb", 8),
+                                   k.get("pl", FAKE), FAKE, FAKE, k.get("npl", FAKE), None)
+    assert app(dt=7) == -1
+    assert app(n=0) == -1
+    assert app(n=200) == -1
+    assert app(blk=0) == -1
+    assert app(kt=None) == -1
+    assert app(npl=ctypes.c_void_p(0x2000), pl=ctypes.c_void_p(0x2000)) == -1  # aliasing
+    assert "alias" in G.graft_last_error()
+    assert app(b=0) == 0

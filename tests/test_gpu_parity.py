@@ -1,8 +1,8 @@
 """GPU parity: the HIP path against the oracle on the same seeded inputs.
 
 Bit-exact: hybrid trees (tokens, parents, positions, masks, node counts,
-firing stage), argmax, accepted paths, and the adjacency table after the
-update.  Attention: max-abs error against the float64 oracle within 1e-2 for
+firing stage), argmax, accepted paths, the adjacency table after the
+update, and the KV cache after the accepted path is committed.  Attention: max-abs error against the float64 oracle within 1e-2 for
 bf16 inputs (fp32 accumulation, bf16 output) and 1e-4 for fp32.
 """
 import sys
@@ -67,7 +67,7 @@ def check_attention(w, out_gpu, tree, rows=None):
 
 def run_full_check(w, attn_rows=None, seed_prompt=False):
     """Whole step on the GPU vs the oracle: build, attention, accept (with a
-    planted path), update."""
+    planted path), update, and the commit of the accepted path to the cache."""
     import torch
     from tree_attention_verification_graft_amd.pipeline import DeviceStep, to_host
     _say(f"[parity] {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
@@ -105,6 +105,15 @@ def run_full_check(w, attn_rows=None, seed_prompt=False):
                                          ref_acc["accept_len"])
     np.testing.assert_array_equal(to_host(ds.m_ids), ref_ids)
     np.testing.assert_array_equal(to_host(ds.m_scores), ref_sc)
+    # commit of the accepted path to the cache (after attention has read it)
+    ds.append()
+    torch.cuda.synchronize()
+    ref_k, ref_v, ref_len = O.append_kv(w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                        w.k_tree, w.v_tree, ref_acc["path_nodes"],
+                                        ref_acc["accept_len"])
+    np.testing.assert_array_equal(to_host(ds.new_prefix_len), ref_len)
+    assert np.array_equal(to_host(ds.k_cache), ref_k), "k_cache after the commit"
+    assert np.array_equal(to_host(ds.v_cache), ref_v), "v_cache after the commit"
     _say(f"[parity] {w.name}: ok, attention max-abs {err:.2e}, "
          f"accept_len {ref_acc['accept_len'].tolist()[:8]}")
     return ds

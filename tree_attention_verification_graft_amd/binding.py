@@ -26,7 +26,7 @@ EXPORTED = [
     "graft_build_tree", "graft_tree_attention_workspace_size",
     "graft_tree_attention", "graft_accept_workspace_size", "graft_accept",
     "graft_update_adjacency_workspace_size", "graft_update_adjacency",
-    "graft_last_error", "graft_version",
+    "graft_append_kv", "graft_last_error", "graft_version",
 ]
 
 
@@ -87,6 +87,7 @@ def _load(path=LIB_PATH):
         "graft_accept": [I, I, I, I, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "graft_update_adjacency_workspace_size": [I, I],
         "graft_update_adjacency": [P, P, I, I, I, I, P, P, P, SZ, P],
+        "graft_append_kv": [I, I, I, I, I, P, P, P, P, I, I, P, I, P, P, P, P, P],
         "graft_last_error": [],
         "graft_version": [],
     }
@@ -249,6 +250,28 @@ def graft_update_adjacency(m_ids, m_scores, path_tokens, accept_len, workspace, 
                                      _ptr(path_tokens), _ptr(accept_len), _ptr(workspace),
                                      ws_bytes, _stream(stream))
     _check(st, "graft_update_adjacency")
+
+
+def graft_append_kv(k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, path_nodes,
+                    accept_len, new_prefix_len, stream=None):
+    B, n_max, hkv, D = k_tree.shape
+    nblk, _, blk, _ = k_cache.shape
+    dt = _dtype_code(k_tree)
+    i32 = torch.int32
+    _expect(v_tree, k_tree.dtype, (B, n_max, hkv, D), "v_tree")
+    _expect(k_cache, k_tree.dtype, (nblk, hkv, blk, D), "k_cache")
+    _expect(v_cache, k_tree.dtype, (nblk, hkv, D, blk), "v_cache")
+    _expect(path_nodes, i32, (B, n_max), "path_nodes")
+    for t, n in ((prefix_len, "prefix_len"), (accept_len, "accept_len"),
+                 (new_prefix_len, "new_prefix_len")):
+        _expect(t, i32, (B,), n)
+    if block_table.dtype != i32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise GraftError("block_table: expected int32 [batch][max_blocks]")
+    st = _lib.graft_append_kv(dt, B, n_max, hkv, D, _ptr(k_tree), _ptr(v_tree), _ptr(k_cache),
+                              _ptr(v_cache), nblk, blk, _ptr(block_table), block_table.shape[1],
+                              _ptr(prefix_len), _ptr(path_nodes), _ptr(accept_len),
+                              _ptr(new_prefix_len), _stream(stream))
+    _check(st, "graft_append_kv")
 
 
 def graft_last_error():

@@ -333,4 +333,48 @@ graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t voc
   return check_launch("graft_update_adjacency");
 }
 
+// ---------------------------------------------------------------- KV append
+graft_status graft_append_kv(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hkv,
+                             int32_t head_dim, const void *k_tree, const void *v_tree,
+                             void *k_cache, void *v_cache, int32_t num_blocks,
+                             int32_t block_size, const int32_t *block_table,
+                             int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                             const int32_t *path_nodes, const int32_t *accept_len,
+                             int32_t *new_prefix_len, hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(dtype == GRAFT_F32 || dtype == GRAFT_BF16, GRAFT_ERR_INVALID_ARG,
+          "graft_append_kv: unknown dtype %d", (int)dtype);
+  REQUIRE(batch >= 0 && n_max >= 1 && n_max <= GRAFT_MAX_NODES && hkv >= 1 && head_dim >= 1,
+          GRAFT_ERR_INVALID_ARG, "graft_append_kv: bad shape");
+  REQUIRE((long long)batch * hkv <= (1LL << 31) - 1, GRAFT_ERR_UNSUPPORTED,
+          "graft_append_kv: batch * hkv too large");
+  REQUIRE(num_blocks >= 0 && block_size >= 1 && max_blocks_per_seq >= 1, GRAFT_ERR_INVALID_ARG,
+          "graft_append_kv: bad cache geometry");
+  if (batch == 0) return GRAFT_OK;
+  REQUIRE(k_tree && v_tree && k_cache && v_cache && block_table && prefix_len && path_nodes &&
+              accept_len && new_prefix_len,
+          GRAFT_ERR_INVALID_ARG, "graft_append_kv: null device pointer");
+  REQUIRE((const void *)new_prefix_len != (const void *)prefix_len, GRAFT_ERR_INVALID_ARG,
+          "graft_append_kv: new_prefix_len must not alias prefix_len");
+  AppendParams p{};
+  p.batch = batch;
+  p.n_max = n_max;
+  p.hkv = hkv;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.k_tree = k_tree;
+  p.v_tree = v_tree;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.prefix_len = prefix_len;
+  p.path_nodes = path_nodes;
+  p.accept_len = accept_len;
+  p.new_prefix_len = new_prefix_len;
+  launch_append_kv(dtype, p, stream);
+  return check_launch("graft_append_kv");
+}
+
 }  // extern "C"

@@ -113,4 +113,19 @@ struct UpdateParams {
 };
 void launch_update(const UpdateParams &p, hipStream_t stream);
 
+// ------------------------------------------------------------ KV append
+struct AppendParams {
+  int32_t batch, n_max, hkv, head_dim, block_size, max_blocks, num_blocks;
+  const void *k_tree;
+  const void *v_tree;
+  void *k_cache;
+  void *v_cache;
+  const int32_t *block_table;
+  const int32_t *prefix_len;
+  const int32_t *path_nodes;
+  const int32_t *accept_len;
+  int32_t *new_prefix_len;
+};
+void launch_append_kv(graft_dtype dtype, const AppendParams &p, hipStream_t stream);
+
 }  // namespace graft

@@ -69,6 +69,7 @@ class DeviceStep:
         self.accept_len = torch.empty((B,), dtype=i32, device=d)
         self.path_nodes = torch.empty((B, self.n_max), dtype=i32, device=d)
         self.path_tokens = torch.empty((B, self.n_max + 1), dtype=i32, device=d)
+        self.new_prefix_len = torch.empty((B,), dtype=i32, device=d)
         # workspaces
         dt = G.GRAFT_BF16 if w.dtype == "bf16" else G.GRAFT_F32
         n = G.graft_tree_attention_workspace_size(dt, B, self.n_max, w.Hq, w.Hkv, w.D,
@@ -102,6 +103,11 @@ class DeviceStep:
     def update(self):
         G.graft_update_adjacency(self.m_ids, self.m_scores, self.path_tokens, self.accept_len,
                                  self.update_ws)
+
+    def append(self):
+        G.graft_append_kv(self.k_tree, self.v_tree, self.k_cache, self.v_cache,
+                          self.block_table, self.prefix_len, self.path_nodes, self.accept_len,
+                          self.new_prefix_len)
 
     def step(self):
         self.build()
