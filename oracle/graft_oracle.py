@@ -456,3 +456,26 @@ def append_kv(k_cache, v_cache, block_table, prefix_len, k_tree, v_tree,
             v[page, :, :, t % blk] = v_tree[b, node, :, :]
         new_len[b] = P + L + 1
     return k, v, new_len
+
+
+def tree_transitions(tree_token, argmax, n_nodes):
+    """Every verified node's transition: (token(i), argmax(i)) for i < n_nodes.
+
+    Reading of the literal wording that M learns from the logits of the
+    verified tree ([AT-method] fourth step): each verified node contributes
+    the target's greedy continuation after its token, accepted or not.  The
+    accepted path's transitions are among them (each accepted node's token is
+    its parent's argmax, and the bonus is the last node's argmax)."""
+    pairs = []
+    for b in range(len(n_nodes)):
+        for i in range(int(n_nodes[b])):
+            pairs.append((int(tree_token[b][i]), int(argmax[b][i])))
+    return pairs
+
+
+def update_adjacency_tree(m_ids, m_scores, tree_token, argmax, n_nodes):
+    """The update of O4 applied to every verified node's transition, as one
+    length-2 path per node."""
+    pairs = tree_transitions(tree_token, argmax, n_nodes)
+    paths = np.array(pairs, dtype=np.int64).reshape(-1, 2)
+    return update_adjacency(m_ids, m_scores, paths, np.zeros(len(paths), np.int64))

@@ -14,6 +14,7 @@ import pytest
 import oracle.graft_oracle as real
 import test_oracle_accept_update as T_au
 import test_oracle_append as T_ap
+import test_oracle_update_tree as T_ut
 import test_oracle_attention as T_at
 import test_oracle_build_tree as T_bt
 
@@ -45,6 +46,8 @@ MUTANTS = [
     ("commit drops the deepest node", "        for j in range(L + 1):\n            node", "        for j in range(L):\n            node"),
     ("commit length short", "new_len[b] = P + L + 1", "new_len[b] = P + L"),
     ("commit V from K", "v[page, :, :, t % blk] = v_tree[b, node, :, :]", "v[page, :, :, t % blk] = k_tree[b, node, :, :]"),
+    ("tree update skips the root", "        for i in range(int(n_nodes[b])):\n            pairs.append", "        for i in range(1, int(n_nodes[b])):\n            pairs.append"),
+    ("tree update pairs reversed", "pairs.append((int(tree_token[b][i]), int(argmax[b][i])))", "pairs.append((int(argmax[b][i]), int(tree_token[b][i])))"),
 ]
 
 
@@ -88,13 +91,18 @@ def _pin_calls():
     for s in range(6):
         calls.append(lambda s=s: T_ap.test_committed_cache_decodes_like_the_verified_row(s))
     calls.append(T_ap.test_root_only_and_capacity)
+    calls.append(T_ut.test_hand_worked_example)
+    for s in range(10):
+        calls.append(lambda s=s: T_ut.test_transitions_against_numpy_argmax_and_path(s))
+    for s in range(6):
+        calls.append(lambda s=s: T_ut.test_update_tree_is_the_update_of_its_pairs(s))
     return calls
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(name, old, new, monkeypatch):
     mod = _mutant_module(old, new)
-    for t in (T_bt, T_at, T_au, T_ap):
+    for t in (T_bt, T_at, T_au, T_ap, T_ut):
         monkeypatch.setattr(t, "O", mod)
     failed = 0
     for call in _pin_calls():
