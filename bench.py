@@ -305,20 +305,23 @@ def main():
         comp.append(e0.elapsed_time(e1) / (reps * CALLS_PER_GRAPH))
     comp_ms = np.array(comp)
 
-    # the next row of the path, measured beside the step: committing the
+    # the next rows of the path, measured beside the step: committing the
     # accepted path's K/V to the cache (idempotent: same slots, same values)
-    g_app = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_app):
-        for k in range(CALLS_PER_GRAPH):
-            sets[k % n_sets].append()
-    g_app.replay()
-    e0, e1 = ev(), ev()
-    e0.record(stream)
-    for _ in range(reps):
-        g_app.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    append_ms = e0.elapsed_time(e1) / (reps * CALLS_PER_GRAPH)
+    # and the all-node update of M
+    next_us = {}
+    for name, call in (("append_kv", "append"), ("update_tree", "update_tree")):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(CALLS_PER_GRAPH):
+                getattr(sets[k % n_sets], call)()
+        g.replay()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        next_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * CALLS_PER_GRAPH)
 
     n_nodes = np.stack([to_host(s.n_nodes) for s in sets])
     tokens = float(n_nodes.sum(axis=1).mean())
@@ -328,7 +331,7 @@ def main():
     achieved = (kv_bytes + qo_bytes) / t_attn_s / 1e9
     kv_gbps = kv_bytes / t_attn_s / 1e9
     traffic = measured_traffic(w.name)
-    log(f"append_kv {append_ms * 1e3:.1f} us per call")
+    log("next rows: " + ", ".join(f"{k} {v:.1f} us" for k, v in next_us.items()))
     log(f"step {ms_per_step * 1e3:.1f} us (eager {ms_eager * 1e3:.1f}); build {comp_ms[0] * 1e3:.1f} attn "
         f"{comp_ms[1] * 1e3:.1f} accept {comp_ms[2] * 1e3:.1f} update "
         f"{comp_ms[3] * 1e3:.1f} us; attention {achieved:.0f} GB/s")
@@ -367,7 +370,7 @@ def main():
             "launch_us": comp_ms[1] * 1e3,
         },
         "cpu_baseline": None,
-        "next_rows_us": {"append_kv": append_ms * 1e3},
+        "next_rows_us": next_us,
     }
     if args.copy_calibration:
         src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)

@@ -13,6 +13,7 @@
  *   graft_tree_attention    verify the hybrid tree with tree-masked attention
  *   graft_accept            greedy (lossless) longest-path acceptance
  *   graft_update_adjacency  online update of the successor table M
+ *   graft_update_adjacency_tree  the same update from every verified node
  *   graft_append_kv         commit of the accepted path to the KV cache
  *
  * Conventions for every call
@@ -243,6 +244,30 @@ graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t voc
                                     int32_t path_stride, const int32_t *path_tokens,
                                     const int32_t *accept_len, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * graft_update_adjacency_tree -- the all-node variant of the online update
+ * (method paragraph, fourth step, read literally: M learns from the logits
+ * of the whole verified tree).  Every verified node i < n_nodes[b]
+ * contributes the transition (tree_token[b][i], argmax[b][i]); the update
+ * rule is that of graft_update_adjacency (counts, batch-synchronous, top_s
+ * by score descending then id ascending).  The accepted path's transitions
+ * are among these.
+ *
+ * tree_token, argmax int32 [batch][n_max] (from graft_build_tree and
+ * graft_accept); n_nodes int32 [batch]; m_ids / m_scores as in
+ * graft_update_adjacency.
+ * workspace: >= graft_update_adjacency_tree_workspace_size(batch, n_max)
+ * bytes, zero-filled before its first use; like graft_update_adjacency,
+ * every call leaves it ready for the next.  Calls that share one workspace
+ * must not overlap.
+ */
+size_t graft_update_adjacency_tree_workspace_size(int32_t batch, int32_t n_max);
+graft_status graft_update_adjacency_tree(int32_t *m_ids, float *m_scores, int32_t vocab,
+                                         int32_t top_s, int32_t batch, int32_t n_max,
+                                         const int32_t *tree_token, const int32_t *argmax,
+                                         const int32_t *n_nodes, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * graft_append_kv -- commit the accepted path to the paged KV cache, the

@@ -26,7 +26,7 @@ def header_functions():
 def test_header_declares_the_calls():
     names = header_functions()
     for n in ["graft_build_tree", "graft_tree_attention", "graft_accept",
-              "graft_update_adjacency", "graft_append_kv"]:
+              "graft_update_adjacency", "graft_update_adjacency_tree", "graft_append_kv"]:
         assert n in names
 
 
@@ -135,3 +135,18 @@ def test_append_kv_validation():
     assert app(npl=ctypes.c_void_p(0x2000), pl=ctypes.c_void_p(0x2000)) == -1  # aliasing
     assert "alias" in G.graft_last_error()
     assert app(b=0) == 0
+
+
+def test_update_tree_validation():
+    def upd(**k):
+        return lib.graft_update_adjacency_tree(FAKE, FAKE, k.get("v", 100), k.get("s", 8),
+                                               k.get("b", 2), k.get("n", 9), FAKE, FAKE, FAKE,
+                                               k.get("ws", FAKE), k.get("wsb", 1 << 20), None)
+    assert upd(n=0) == -1
+    assert upd(n=200) == -1
+    assert upd(s=0) == -1
+    assert upd(v=0) == -1
+    assert upd(wsb=8) == -3
+    assert upd(ws=None) == -3
+    assert upd(b=0) == 0
+    assert lib.graft_update_adjacency_tree_workspace_size(2, 9) >= 2 * 9 * 12

@@ -239,3 +239,41 @@ def test_full_size(name):
                                    np.array([len(w.prompt) - 2]))[0]
     rows = _sample_rows(w, oracle_tree(w, m_ids), 48, 7)
     run_full_check(w, attn_rows=rows, seed_prompt=seed)
+
+
+UPDATE_TREE = [(n, SMALL[n]) for n in W.CONFIG_ORDER] + [
+    # more than 1024 verified nodes: the hash-table path of the update
+    ("qwen3_8b_b16", dict(B=16, Hq=8, Hkv=2, prefix=(40, 300), V=4096)),
+]
+
+
+@pytest.mark.parametrize("name,over", UPDATE_TREE,
+                         ids=[f"{n}-{i}" for i, (n, _) in enumerate(UPDATE_TREE)])
+def test_update_tree_small_variant(name, over):
+    """The all-node update on the GPU against the oracle, from the same M:
+    every verified node's (token, argmax) transition."""
+    import torch
+    from tree_attention_verification_graft_amd.pipeline import DeviceStep, to_host
+    w = W.make(name, **over)
+    m_ids, m_scores = w.m_ids, w.m_scores
+    if w.prompt is not None:
+        m_ids, m_scores = O.update_adjacency(m_ids, m_scores, w.prompt[None],
+                                             np.array([len(w.prompt) - 2]))
+    ref_tree = oracle_tree(w, m_ids)
+    logits = W.plant_path(w.logits, w.dtype, ref_tree["token"], ref_tree["parent"],
+                          ref_tree["n_nodes"], w.plant_seed)
+    ds = DeviceStep(w, logits=logits, alloc_update_for_prompt=w.prompt is not None)
+    if w.prompt is not None:
+        ds.seed_from_prompt(w.prompt)
+    ds.build()
+    ds.accept()
+    ds.update_tree()
+    torch.cuda.synchronize()
+    ref_acc = O.accept(logits, w.dtype, ref_tree["token"], ref_tree["parent"],
+                       ref_tree["n_nodes"])
+    ref_ids, ref_sc = O.update_adjacency_tree(m_ids, m_scores, ref_tree["token"],
+                                              ref_acc["argmax"], ref_tree["n_nodes"])
+    np.testing.assert_array_equal(to_host(ds.m_ids), ref_ids)
+    np.testing.assert_array_equal(to_host(ds.m_scores), ref_sc)
+    _say(f"[parity] {w.name}: all-node update ok "
+         f"({int(ref_tree['n_nodes'].sum())} transitions)")

@@ -26,6 +26,7 @@ EXPORTED = [
     "graft_build_tree", "graft_tree_attention_workspace_size",
     "graft_tree_attention", "graft_accept_workspace_size", "graft_accept",
     "graft_update_adjacency_workspace_size", "graft_update_adjacency",
+    "graft_update_adjacency_tree_workspace_size", "graft_update_adjacency_tree",
     "graft_append_kv", "graft_last_error", "graft_version",
 ]
 
@@ -87,6 +88,8 @@ def _load(path=LIB_PATH):
         "graft_accept": [I, I, I, I, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "graft_update_adjacency_workspace_size": [I, I],
         "graft_update_adjacency": [P, P, I, I, I, I, P, P, P, SZ, P],
+        "graft_update_adjacency_tree_workspace_size": [I, I],
+        "graft_update_adjacency_tree": [P, P, I, I, I, I, P, P, P, P, SZ, P],
         "graft_append_kv": [I, I, I, I, I, P, P, P, P, I, I, P, I, P, P, P, P, P],
         "graft_last_error": [],
         "graft_version": [],
@@ -250,6 +253,27 @@ def graft_update_adjacency(m_ids, m_scores, path_tokens, accept_len, workspace, 
                                      _ptr(path_tokens), _ptr(accept_len), _ptr(workspace),
                                      ws_bytes, _stream(stream))
     _check(st, "graft_update_adjacency")
+
+
+def graft_update_adjacency_tree_workspace_size(batch, n_max):
+    return int(_lib.graft_update_adjacency_tree_workspace_size(batch, n_max))
+
+
+def graft_update_adjacency_tree(m_ids, m_scores, tree_token, argmax, n_nodes, workspace,
+                                stream=None):
+    V, S = m_ids.shape
+    B, n_max = tree_token.shape
+    i32 = torch.int32
+    _expect(m_ids, i32, (V, S), "m_ids")
+    _expect(m_scores, torch.float32, (V, S), "m_scores")
+    _expect(argmax, i32, (B, n_max), "argmax")
+    _expect(tree_token, i32, (B, n_max), "tree_token")
+    _expect(n_nodes, i32, (B,), "n_nodes")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.graft_update_adjacency_tree(_ptr(m_ids), _ptr(m_scores), V, S, B, n_max,
+                                          _ptr(tree_token), _ptr(argmax), _ptr(n_nodes),
+                                          _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "graft_update_adjacency_tree")
 
 
 def graft_append_kv(k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, path_nodes,

@@ -11,9 +11,10 @@
 // depend on the order in which atomics land.  Each kernel clears the
 // workspace entries it consumed, so the workspace is all-zero between calls.
 //
-// Calls with at most 4096 potential transitions (one decode step) take a
-// path that sorts the pairs in LDS instead and needs no workspace; both
-// paths give the same table.
+// Calls with at most 4096 potential transitions (one decode step; callers
+// whose transitions are nearly all valid lower that limit) take a path that
+// sorts the pairs in LDS instead and needs no workspace; both paths give the
+// same table.
 //
 // Method: "Draft Less, Retrieve More" (aitrends.kr summary), method paragraph
 // (fourth step: online update of M from the verified tree; fifth step:
@@ -494,7 +495,32 @@ __global__ __launch_bounds__(kSmallThreads) void update_small_kernel(UpdateParam
   }
 }
 
+// The all-node variant: every verified node's (token, argmax) as one
+// length-2 path; rows past n_nodes get accept length -1 (skipped).
+__global__ __launch_bounds__(kThreads) void tree_pairs_kernel(int32_t batch, int32_t n_max,
+                                                             const int32_t *tree_token,
+                                                             const int32_t *argmax,
+                                                             const int32_t *n_nodes,
+                                                             int32_t *pairs, int32_t *lens) {
+  const long r = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= (long)batch * n_max) return;
+  const int b = (int)(r / n_max), i = (int)(r % n_max);
+  const bool live = i < min(n_nodes[b], n_max);
+  pairs[2 * r] = live ? tree_token[r] : -1;
+  pairs[2 * r + 1] = live ? argmax[r] : -1;
+  lens[r] = live ? 0 : -1;
+}
+
 }  // namespace
+
+void launch_tree_pairs(int32_t batch, int32_t n_max, const int32_t *tree_token,
+                       const int32_t *argmax, const int32_t *n_nodes, int32_t *pairs,
+                       int32_t *lens, hipStream_t stream) {
+  const long rows = (long)batch * n_max;
+  hipLaunchKernelGGL(tree_pairs_kernel, dim3((unsigned)((rows + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, batch, n_max, tree_token, argmax, n_nodes, pairs,
+                     lens);
+}
 
 UpdateLayout update_layout(uint32_t capacity) {
   UpdateLayout l{};
@@ -521,8 +547,8 @@ UpdateLayout update_layout(uint32_t capacity) {
   return l;
 }
 
-void launch_update(const UpdateParams &p, hipStream_t stream) {
-  if (p.max_transitions <= kSmallT) {
+void launch_update(const UpdateParams &p, hipStream_t stream, int32_t small_limit) {
+  if (p.max_transitions <= std::min(small_limit, kSmallT)) {
     // enough workgroups that every touched row (at most one per transition)
     // gets a wave of its own
     const int groups = std::max(1, std::min(64, (p.max_transitions + kSmallWaves - 1) / kSmallWaves));

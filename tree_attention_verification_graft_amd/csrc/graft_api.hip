@@ -292,11 +292,11 @@ size_t graft_update_adjacency_workspace_size(int32_t n_paths, int32_t path_strid
   return update_layout(update_capacity(t)).total;
 }
 
-graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t vocab,
-                                    int32_t top_s, int32_t n_paths, int32_t path_stride,
-                                    const int32_t *path_tokens, const int32_t *accept_len,
-                                    void *workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+static graft_status update_impl(int32_t *m_ids, float *m_scores, int32_t vocab, int32_t top_s,
+                                int32_t n_paths, int32_t path_stride,
+                                const int32_t *path_tokens, const int32_t *accept_len,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                int32_t small_limit) {
   g_error[0] = 0;
   REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_update_adjacency: vocab < 1");
   REQUIRE(top_s >= 1 && top_s <= GRAFT_MAX_TOP_S, GRAFT_ERR_INVALID_ARG,
@@ -329,8 +329,62 @@ graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t voc
   p.accept_len = accept_len;
   p.ws = static_cast<char *>(workspace);
   p.lay = update_layout(cap);
-  launch_update(p, stream);
+  launch_update(p, stream, small_limit);
   return check_launch("graft_update_adjacency");
+}
+
+graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t vocab,
+                                    int32_t top_s, int32_t n_paths, int32_t path_stride,
+                                    const int32_t *path_tokens, const int32_t *accept_len,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  return update_impl(m_ids, m_scores, vocab, top_s, n_paths, path_stride, path_tokens,
+                     accept_len, workspace, workspace_bytes, stream, 4096);
+}
+
+// ------------------------------------------------------- all-node update
+static size_t tree_pairs_bytes(int32_t batch, int32_t n_max) {
+  const size_t rows = (size_t)batch * n_max;
+  return align_up(rows * 2 * sizeof(int32_t), 256) + align_up(rows * sizeof(int32_t), 256);
+}
+
+size_t graft_update_adjacency_tree_workspace_size(int32_t batch, int32_t n_max) {
+  if (batch < 0 || n_max < 1 || n_max > GRAFT_MAX_NODES) return 0;
+  return tree_pairs_bytes(batch, n_max) +
+         graft_update_adjacency_workspace_size(batch * n_max, 2);
+}
+
+graft_status graft_update_adjacency_tree(int32_t *m_ids, float *m_scores, int32_t vocab,
+                                         int32_t top_s, int32_t batch, int32_t n_max,
+                                         const int32_t *tree_token, const int32_t *argmax,
+                                         const int32_t *n_nodes, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(batch >= 0 && n_max >= 1 && n_max <= GRAFT_MAX_NODES, GRAFT_ERR_INVALID_ARG,
+          "graft_update_adjacency_tree: batch/n_max out of range");
+  REQUIRE((long long)batch * n_max <= (1LL << 28), GRAFT_ERR_UNSUPPORTED,
+          "graft_update_adjacency_tree: batch * n_max too large");
+  REQUIRE(vocab >= 1 && top_s >= 1 && top_s <= GRAFT_MAX_TOP_S, GRAFT_ERR_INVALID_ARG,
+          "graft_update_adjacency_tree: vocab/top_s out of range");
+  if (batch == 0) return GRAFT_OK;
+  REQUIRE(m_ids && m_scores && tree_token && argmax && n_nodes, GRAFT_ERR_INVALID_ARG,
+          "graft_update_adjacency_tree: null device pointer");
+  const size_t need = graft_update_adjacency_tree_workspace_size(batch, n_max);
+  REQUIRE(workspace && workspace_bytes >= need, GRAFT_ERR_WORKSPACE,
+          "graft_update_adjacency_tree: workspace of %zu bytes needed, %zu given", need,
+          workspace_bytes);
+  char *ws = static_cast<char *>(workspace);
+  int32_t *pairs = reinterpret_cast<int32_t *>(ws);
+  int32_t *lens = reinterpret_cast<int32_t *>(
+      ws + align_up((size_t)batch * n_max * 2 * sizeof(int32_t), 256));
+  launch_tree_pairs(batch, n_max, tree_token, argmax, n_nodes, pairs, lens, stream);
+  const graft_status st = check_launch("graft_update_adjacency_tree");
+  if (st != GRAFT_OK) return st;
+  const size_t head = tree_pairs_bytes(batch, n_max);
+  // nearly every row is a valid transition here: past 1024 of them the
+  // hash-table path is faster than sorting them in every workgroup
+  return update_impl(m_ids, m_scores, vocab, top_s, batch * n_max, 2, pairs, lens, ws + head,
+                     workspace_bytes - head, stream, 1024);
 }
 
 // ---------------------------------------------------------------- KV append

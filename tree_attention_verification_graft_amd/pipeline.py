@@ -81,6 +81,8 @@ class DeviceStep:
         if alloc_update_for_prompt and w.prompt is not None:
             n = max(n, G.graft_update_adjacency_workspace_size(1, len(w.prompt)))
         self.update_ws = torch.zeros(n, dtype=torch.uint8, device=d)
+        n = G.graft_update_adjacency_tree_workspace_size(B, self.n_max)
+        self.update_tree_ws = torch.zeros(n, dtype=torch.uint8, device=d)
 
     # ---- the four calls
     def build(self):
@@ -103,6 +105,12 @@ class DeviceStep:
     def update(self):
         G.graft_update_adjacency(self.m_ids, self.m_scores, self.path_tokens, self.accept_len,
                                  self.update_ws)
+
+    def update_tree(self):
+        """The all-node variant of the update (every verified node's
+        transition) in place of the accepted-path update."""
+        G.graft_update_adjacency_tree(self.m_ids, self.m_scores, self.tree_token, self.argmax,
+                                      self.n_nodes, self.update_tree_ws)
 
     def append(self):
         G.graft_append_kv(self.k_tree, self.v_tree, self.k_cache, self.v_cache,
