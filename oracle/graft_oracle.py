@@ -29,7 +29,8 @@ Where the pages leave a step open, the reading taken is stated in the function
 that implements it; the full list of readings lives with the design notes.
 
 O5 (append_kv) commits the accepted path to the KV cache, the step that
-follows verification when decoding continues.
+follows verification when decoding continues; O6 (accept_sample) is the
+temperature > 0 acceptance.
 
 Conventions shared with the C header (by specification, not by code):
   * draft arrays  [B][n_draft_max]: parent (-1 = child of the root; otherwise
@@ -479,3 +480,83 @@ def update_adjacency_tree(m_ids, m_scores, tree_token, argmax, n_nodes):
     pairs = tree_transitions(tree_token, argmax, n_nodes)
     paths = np.array(pairs, dtype=np.int64).reshape(-1, 2)
     return update_adjacency(m_ids, m_scores, paths, np.zeros(len(paths), np.int64))
+
+
+# ----------------------------------------------------------------------------
+# O6: lossless sampling acceptance  ([AT-arch] retrieval nodes are proposals
+# like drafts and verification preserves the target distribution; [CP]
+# lossless), the temperature > 0 counterpart of O3
+# ----------------------------------------------------------------------------
+
+def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_parent,
+                  n_nodes, rand_accept, rand_sample):
+    """Recursive rejection sampling over the verified tree.
+
+    Reading: every child of a node is a deterministic proposal of its token,
+    tried in index order against the node's target distribution
+    p = softmax(logits / T).  With residual r (initially p), a proposal of
+    token x is accepted iff rand_accept[b][child] < r(x); on rejection x's
+    mass is removed and r renormalised (r(x) = 0 afterwards, so a repeated
+    token is always rejected).  An accepted child becomes the current node;
+    when no child is accepted, the bonus token is the smallest y whose
+    cumulative residual mass exceeds rand_sample[b][node] (inverse CDF over
+    token ids in increasing order).  The emitted tokens are distributed as
+    the target's own samples, whatever the proposals (lossless).
+
+    All arithmetic is float64 from the exact logits.  Returns accept_len,
+    path_nodes, path_tokens like `accept`, plus `margin`: per sequence, the
+    smallest relative distance of a random number from the threshold it was
+    compared with (decisions closer than float32 rounding are ambiguous)."""
+    lg = as_f64(np.asarray(logits), dtype)
+    B, n_max, V = lg.shape
+    T = float(temperature)
+    accept_len = np.zeros(B, np.int32)
+    path_nodes = np.full((B, n_max), -1, np.int32)
+    path_tokens = np.full((B, n_max + 1), -1, np.int32)
+    margin = np.full(B, np.inf)
+    for b in range(B):
+        n = int(n_nodes[b])
+        node = 0
+        path = [0]
+        while True:
+            z = lg[b, node] / T
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            removed = 0.0
+            gone = set()
+            nxt = -1
+            for c in range(node + 1, n):
+                if int(tree_parent[b, c]) != node:
+                    continue
+                x = int(tree_token[b, c])
+                if x in gone:
+                    continue
+                thr = p[x] / (1.0 - removed) if removed < 1.0 else 0.0
+                u = float(rand_accept[b, c])
+                margin[b] = min(margin[b], abs(u - thr) / max(thr, 1e-300))
+                if u < thr:
+                    nxt = c
+                    break
+                gone.add(x)
+                removed += p[x]
+            if nxt < 0:
+                r = p.copy()
+                for x in gone:
+                    r[x] = 0.0
+                cdf = np.cumsum(r)
+                target = float(rand_sample[b, node]) * cdf[-1]
+                y = int(np.searchsorted(cdf, target, side="right"))
+                y = min(y, V - 1)
+                lo = cdf[y - 1] if y > 0 else 0.0
+                m = min(abs(target - lo), abs(cdf[y] - target))
+                margin[b] = min(margin[b], m / max(cdf[-1], 1e-300))
+                bonus = y
+                break
+            node = nxt
+            path.append(node)
+        accept_len[b] = len(path) - 1
+        path_nodes[b, :len(path)] = path
+        path_tokens[b, :len(path)] = [int(tree_token[b, x]) for x in path]
+        path_tokens[b, len(path)] = bonus
+    return {"accept_len": accept_len, "path_nodes": path_nodes,
+            "path_tokens": path_tokens, "margin": margin}

@@ -14,6 +14,7 @@ import pytest
 import oracle.graft_oracle as real
 import test_oracle_accept_update as T_au
 import test_oracle_append as T_ap
+import test_oracle_sample as T_sa
 import test_oracle_update_tree as T_ut
 import test_oracle_attention as T_at
 import test_oracle_build_tree as T_bt
@@ -48,6 +49,10 @@ MUTANTS = [
     ("commit V from K", "v[page, :, :, t % blk] = v_tree[b, node, :, :]", "v[page, :, :, t % blk] = k_tree[b, node, :, :]"),
     ("tree update skips the root", "        for i in range(int(n_nodes[b])):\n            pairs.append", "        for i in range(1, int(n_nodes[b])):\n            pairs.append"),
     ("tree update pairs reversed", "pairs.append((int(tree_token[b][i]), int(argmax[b][i])))", "pairs.append((int(argmax[b][i]), int(tree_token[b][i])))"),
+    ("sampling test against p, not the residual", "thr = p[x] / (1.0 - removed) if removed < 1.0 else 0.0", "thr = p[x]"),
+    ("bonus keeps rejected mass", "                    r[x] = 0.0\n", "                    r[x] = r[x]\n"),
+    ("sampling accepts on u > r(x)", "                if u < thr:\n", "                if u > thr:\n"),
+    ("bonus from the root's row", "                r = p.copy()\n", "                r = np.exp(lg[b, 0] / T - (lg[b, 0] / T).max()); r /= r.sum()\n"),
 ]
 
 
@@ -96,13 +101,18 @@ def _pin_calls():
         calls.append(lambda s=s: T_ut.test_transitions_against_numpy_argmax_and_path(s))
     for s in range(6):
         calls.append(lambda s=s: T_ut.test_update_tree_is_the_update_of_its_pairs(s))
+    calls += [T_sa.test_root_only_is_inverse_cdf_sampling,
+              T_sa.test_repeated_sibling_token_never_accepted]
+    for s in range(10):
+        calls.append(lambda s=s: T_sa.test_low_temperature_is_greedy(s))
+    calls.append(T_sa.test_lossless_first_and_second_token)
     return calls
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(name, old, new, monkeypatch):
     mod = _mutant_module(old, new)
-    for t in (T_bt, T_at, T_au, T_ap, T_ut):
+    for t in (T_bt, T_at, T_au, T_ap, T_ut, T_sa):
         monkeypatch.setattr(t, "O", mod)
     failed = 0
     for call in _pin_calls():
