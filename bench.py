@@ -230,6 +230,10 @@ def main():
                           w.plant_seed)
     base.logits.copy_(torch.from_numpy(logits.view(np.int16) if logits.dtype == np.uint16
                                        else logits).to(dev).view(base.logits.dtype))
+    # the random numbers of sampling acceptance (timed beside the step)
+    ra, rs = W.sampling_uniforms(w.plant_seed, w.B, base.n_max)
+    base.rand_accept.copy_(torch.from_numpy(ra).to(dev))
+    base.rand_sample.copy_(torch.from_numpy(rs).to(dev))
     per_set = sum(x.numel() * x.element_size() for x in
                   (base.q, base.k_tree, base.v_tree, base.k_cache, base.v_cache, base.logits))
     n_sets = max(1, math.ceil(ROTATE_BYTES / per_set))
@@ -306,14 +310,17 @@ def main():
     comp_ms = np.array(comp)
 
     # the next rows of the path, measured beside the step: committing the
-    # accepted path's K/V to the cache (idempotent: same slots, same values)
-    # and the all-node update of M
+    # accepted path's K/V to the cache (idempotent: same slots, same values),
+    # the all-node update of M, and sampling acceptance at temperature 1
+    # (last: it overwrites the accepted paths)
     next_us = {}
-    for name, call in (("append_kv", "append"), ("update_tree", "update_tree")):
+    for name, call in (("append_kv", lambda s: s.append()),
+                       ("update_tree", lambda s: s.update_tree()),
+                       ("accept_sample", lambda s: s.accept_sample(1.0))):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for k in range(CALLS_PER_GRAPH):
-                getattr(sets[k % n_sets], call)()
+                call(sets[k % n_sets])
         g.replay()
         e0, e1 = ev(), ev()
         e0.record(stream)

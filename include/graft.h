@@ -12,6 +12,7 @@
  *   graft_build_tree        prune the draft tree and refill it from M
  *   graft_tree_attention    verify the hybrid tree with tree-masked attention
  *   graft_accept            greedy (lossless) longest-path acceptance
+ *   graft_accept_sample     sampling (temperature > 0) lossless acceptance
  *   graft_update_adjacency  online update of the successor table M
  *   graft_update_adjacency_tree  the same update from every verified node
  *   graft_append_kv         commit of the accepted path to the KV cache
@@ -212,6 +213,52 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max,
                           int32_t *path_nodes, int32_t *path_tokens,
                           void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * graft_accept_sample -- lossless acceptance when the target samples at
+ * temperature T > 0 (architecture paragraph: retrieval nodes are proposals
+ * like drafts and verification keeps the target distribution; abstract:
+ * lossless), by recursive rejection sampling.
+ *
+ * Each node's target distribution is p = softmax(logits[b][i] / T).  From
+ * the root, the children of the current node are tried in index order, each
+ * as a deterministic proposal of its token x: with r the residual
+ * distribution (initially p), the child is accepted iff
+ * rand_accept[b][child] < r(x); otherwise x's mass is removed from r and r
+ * renormalised (so a token repeated among siblings is never accepted).  An
+ * accepted child becomes the current node.  When no child is accepted, the
+ * bonus token is the smallest y whose cumulative residual mass, over token
+ * ids in increasing order, exceeds rand_sample[b][node] * (total residual
+ * mass).  The emitted tokens are distributed as samples of the target.
+ *
+ *   accept_len, path_nodes, path_tokens  as graft_accept (the last valid
+ *                   path_tokens entry is the sampled bonus token)
+ * Inputs: logits [batch][n_max][vocab] (dtype), finite or -inf;
+ * temperature finite and > 0; tree_token, tree_parent int32 [batch][n_max]
+ * and n_nodes int32 [batch] as produced by graft_build_tree; rand_accept,
+ * rand_sample float32 [batch][n_max] in [0, 1), drawn by the caller (entry
+ * [b][i] of rand_accept is child i's test, of rand_sample node i's bonus
+ * draw).  Precision: the acceptance tests use probabilities from float32
+ * exponentials (relative error below about 1.5e-6), so a test can differ
+ * from exact arithmetic only when |u (1 - removed) - p(x)| is below a few
+ * 1e-6; the bonus draw uses float64 masses and sums, so it can differ only
+ * when rand_sample * (residual mass) lies within about 1e-13 (relative) of
+ * a token's cumulative boundary.
+ * workspace: >= graft_accept_sample_workspace_size(...) bytes, any contents
+ * (per-chunk row statistics, per-chunk residual masses of the stop row and
+ * a per-sequence record between the launches).  Calls that share one
+ * workspace must not overlap.
+ */
+size_t graft_accept_sample_workspace_size(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                          int32_t vocab);
+graft_status graft_accept_sample(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                 int32_t vocab, const void *logits, float temperature,
+                                 const int32_t *tree_token, const int32_t *tree_parent,
+                                 const int32_t *n_nodes, const float *rand_accept,
+                                 const float *rand_sample, int32_t *accept_len,
+                                 int32_t *path_nodes, int32_t *path_tokens,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * graft_update_adjacency -- online update of M (method paragraph, fourth

@@ -504,16 +504,22 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
     the target's own samples, whatever the proposals (lossless).
 
     All arithmetic is float64 from the exact logits.  Returns accept_len,
-    path_nodes, path_tokens like `accept`, plus `margin`: per sequence, the
-    smallest relative distance of a random number from the threshold it was
-    compared with (decisions closer than float32 rounding are ambiguous)."""
+    path_nodes, path_tokens like `accept`, plus two diagnostics per
+    sequence that say how close each decision came to going the other way:
+    `margin_accept`, the smallest |u * (1 - removed) - p(x)| over the child
+    tests (the test u < r(x) in absolute probability units), and
+    `margin_bonus`, the distance of the bonus draw's target from the nearest
+    boundary of the sampled token's CDF interval, relative to the residual
+    mass.  An implementation whose probabilities carry an error below a
+    margin takes the same decision."""
     lg = as_f64(np.asarray(logits), dtype)
     B, n_max, V = lg.shape
     T = float(temperature)
     accept_len = np.zeros(B, np.int32)
     path_nodes = np.full((B, n_max), -1, np.int32)
     path_tokens = np.full((B, n_max + 1), -1, np.int32)
-    margin = np.full(B, np.inf)
+    margin_accept = np.full(B, np.inf)
+    margin_bonus = np.full(B, np.inf)
     for b in range(B):
         n = int(n_nodes[b])
         node = 0
@@ -533,7 +539,7 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
                     continue
                 thr = p[x] / (1.0 - removed) if removed < 1.0 else 0.0
                 u = float(rand_accept[b, c])
-                margin[b] = min(margin[b], abs(u - thr) / max(thr, 1e-300))
+                margin_accept[b] = min(margin_accept[b], abs(u * (1.0 - removed) - p[x]))
                 if u < thr:
                     nxt = c
                     break
@@ -549,7 +555,7 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
                 y = min(y, V - 1)
                 lo = cdf[y - 1] if y > 0 else 0.0
                 m = min(abs(target - lo), abs(cdf[y] - target))
-                margin[b] = min(margin[b], m / max(cdf[-1], 1e-300))
+                margin_bonus[b] = min(margin_bonus[b], m / max(cdf[-1], 1e-300))
                 bonus = y
                 break
             node = nxt
@@ -559,4 +565,5 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
         path_tokens[b, :len(path)] = [int(tree_token[b, x]) for x in path]
         path_tokens[b, len(path)] = bonus
     return {"accept_len": accept_len, "path_nodes": path_nodes,
-            "path_tokens": path_tokens, "margin": margin}
+            "path_tokens": path_tokens, "margin_accept": margin_accept,
+            "margin_bonus": margin_bonus}

@@ -26,7 +26,8 @@ def header_functions():
 def test_header_declares_the_calls():
     names = header_functions()
     for n in ["graft_build_tree", "graft_tree_attention", "graft_accept",
-              "graft_update_adjacency", "graft_update_adjacency_tree", "graft_append_kv"]:
+              "graft_accept_sample", "graft_update_adjacency", "graft_update_adjacency_tree",
+              "graft_append_kv"]:
         assert n in names
 
 
@@ -150,3 +151,34 @@ def test_update_tree_validation():
     assert upd(ws=None) == -3
     assert upd(b=0) == 0
     assert lib.graft_update_adjacency_tree_workspace_size(2, 9) >= 2 * 9 * 12
+
+
+def test_accept_sample_validation():
+    def acc(**k):
+        return lib.graft_accept_sample(k.get("dt", 1), k.get("b", 2), k.get("n", 17),
+                                       k.get("v", 1000), k.get("lg", FAKE),
+                                       ctypes.c_float(k.get("t", 0.7)), *([FAKE] * 8),
+                                       k.get("ws", FAKE), k.get("wsb", 1 << 20), None)
+    assert acc(dt=3) == -1
+    assert acc(n=0) == -1
+    assert acc(n=129) == -1
+    assert acc(v=0) == -1
+    assert acc(t=0.0) == -1
+    assert acc(t=-1.0) == -1
+    assert acc(t=float("inf")) == -1
+    assert acc(t=float("nan")) == -1
+    assert "temperature" in G.graft_last_error()
+    assert acc(t=1e-38) == -2             # log2(e) / T beyond float range
+    assert acc(lg=None) == -1
+    assert acc(wsb=8) == -3
+    assert acc(ws=None) == -3
+    assert acc(b=0) == 0
+    align = lambda x: -(-x // 256) * 256
+    # a 16-byte (float max, float64 sum) record per (row, vocab chunk of
+    # 4096 bf16 or 2048 f32 entries), a float64 mass per (sequence, chunk)
+    # of the stop row, and a 544-byte hand-over record per sequence
+    for dt, ch in ((1, 38), (0, 75)):
+        want = align(2 * 65 * ch * 16) + align(2 * ch * 8) + align(2 * 544)
+        assert lib.graft_accept_sample_workspace_size(dt, 2, 65, 151936) == want
+    assert acc(v=2304 * 4096 + 1) == -2   # more chunks than one workgroup stages
+    assert lib.graft_accept_sample_workspace_size(5, 2, 65, 151936) == 0

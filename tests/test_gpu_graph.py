@@ -68,3 +68,36 @@ def test_step_graph_replays_match_eager(name, over):
         got = _snapshot(ds)
         for k, v in ref.items():
             assert torch.equal(got[k], v), f"replay {rep}: {k} differs from the eager step"
+
+
+def test_sampling_acceptance_graph_replays_match_eager():
+    """Sampling acceptance (two launches, no memsets) captured once and
+    replayed: every replay equals the eager call bit for bit."""
+    import torch
+    from tree_attention_verification_graft_amd.pipeline import DeviceStep, to_device
+    w = W.make("qwen3_8b_b16", B=4, Hq=8, Hkv=2, prefix=(300, 900), V=5000)
+    ds = DeviceStep(w)
+    ds.build()
+    torch.cuda.synchronize()
+    t = ds.tree_host()
+    logits = W.plant_path(w.logits, w.dtype, t["token"], t["parent"], t["n_nodes"],
+                          w.plant_seed, boost=4.0)
+    ds.logits.copy_(to_device(logits, "cuda"))
+    ra, rs = W.sampling_uniforms(9, w.B, ds.n_max)
+    ds.rand_accept.copy_(to_device(ra, "cuda"))
+    ds.rand_sample.copy_(to_device(rs, "cuda"))
+    ds.accept_sample(0.8)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (ds.accept_len, ds.path_nodes, ds.path_tokens)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ds.accept_sample(0.8)
+    for rep in range(3):
+        for x in (ds.accept_len, ds.path_nodes, ds.path_tokens):
+            x.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("accept_len", "path_nodes", "path_tokens"), ref,
+                              (ds.accept_len, ds.path_nodes, ds.path_tokens)):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"

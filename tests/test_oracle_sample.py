@@ -122,3 +122,25 @@ def test_repeated_sibling_token_never_accepted():
                         np.array([[0.5, 0.5, 0.5]]))
     assert r["accept_len"][0] == 0
     assert r["path_tokens"][0, 1] != 2
+
+
+def test_margins_on_a_hand_worked_case():
+    """Root with children of tokens 0 and 1 under p = (0.5, 0.3, 0.15, 0.05):
+    u = 0.55 rejects token 0 (margin 0.05); with 0.5 removed, u = 0.56 gives
+    0.56 * 0.5 - 0.3 = -0.02, so token 1 is accepted (margin 0.02).  Node 2
+    has no children; its uniform row and draw 0.6 pick token 2, whose CDF
+    interval [0.5, 0.75) lies 0.1 from the target at its nearer end."""
+    p_root = np.array([0.5, 0.3, 0.15, 0.05])
+    logits = np.zeros((1, 3, 4), np.float32)
+    logits[0, 0] = np.log(p_root)
+    parent = np.array([[-1, 0, 0]], np.int32)
+    token = np.array([[3, 0, 1]], np.int32)
+    ra = np.array([[0.0, 0.55, 0.56]])
+    rs = np.array([[0.0, 0.0, 0.6]])
+    r = O.accept_sample(logits, "f32", 1.0, token, parent, np.array([3]), ra, rs)
+    assert r["accept_len"][0] == 1
+    assert list(r["path_nodes"][0]) == [0, 2, -1]
+    assert list(r["path_tokens"][0]) == [3, 1, 2, -1]
+    # float32 logits of log(p) carry ~1e-8 relative error
+    assert abs(r["margin_accept"][0] - 0.02) < 1e-6
+    assert abs(r["margin_bonus"][0] - 0.1) < 1e-6

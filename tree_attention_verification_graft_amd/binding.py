@@ -25,6 +25,7 @@ MAX_TOP_S = 32
 EXPORTED = [
     "graft_build_tree", "graft_tree_attention_workspace_size",
     "graft_tree_attention", "graft_accept_workspace_size", "graft_accept",
+    "graft_accept_sample_workspace_size", "graft_accept_sample",
     "graft_update_adjacency_workspace_size", "graft_update_adjacency",
     "graft_update_adjacency_tree_workspace_size", "graft_update_adjacency_tree",
     "graft_append_kv", "graft_last_error", "graft_version",
@@ -86,6 +87,9 @@ def _load(path=LIB_PATH):
                                  ctypes.c_float, P, P, SZ, P],
         "graft_accept_workspace_size": [I, I, I],
         "graft_accept": [I, I, I, I, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "graft_accept_sample_workspace_size": [I, I, I, I],
+        "graft_accept_sample": [I, I, I, I, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, SZ,
+                                P],
         "graft_update_adjacency_workspace_size": [I, I],
         "graft_update_adjacency": [P, P, I, I, I, I, P, P, P, SZ, P],
         "graft_update_adjacency_tree_workspace_size": [I, I],
@@ -235,6 +239,34 @@ def graft_accept(logits, tree_token, tree_parent, tree_mask, n_nodes, argmax, ac
                            _ptr(path_nodes), _ptr(path_tokens), _ptr(workspace), ws_bytes,
                            _stream(stream))
     _check(st, "graft_accept")
+
+
+def graft_accept_sample_workspace_size(dtype, batch, n_max, vocab):
+    code = GRAFT_BF16 if dtype in ("bf16", torch.bfloat16) else GRAFT_F32
+    return int(_lib.graft_accept_sample_workspace_size(code, batch, n_max, vocab))
+
+
+def graft_accept_sample(logits, temperature, tree_token, tree_parent, n_nodes, rand_accept,
+                        rand_sample, accept_len, path_nodes, path_tokens, workspace,
+                        stream=None):
+    B, n_max, V = logits.shape
+    dt = _dtype_code(logits)
+    i32 = torch.int32
+    for t, n in ((tree_token, "tree_token"), (tree_parent, "tree_parent"),
+                 (path_nodes, "path_nodes")):
+        _expect(t, i32, (B, n_max), n)
+    _expect(rand_accept, torch.float32, (B, n_max), "rand_accept")
+    _expect(rand_sample, torch.float32, (B, n_max), "rand_sample")
+    _expect(path_tokens, i32, (B, n_max + 1), "path_tokens")
+    _expect(accept_len, i32, (B,), "accept_len")
+    _expect(n_nodes, i32, (B,), "n_nodes")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.graft_accept_sample(dt, B, n_max, V, _ptr(logits), float(temperature),
+                                  _ptr(tree_token), _ptr(tree_parent), _ptr(n_nodes),
+                                  _ptr(rand_accept), _ptr(rand_sample), _ptr(accept_len),
+                                  _ptr(path_nodes), _ptr(path_tokens), _ptr(workspace),
+                                  ws_bytes, _stream(stream))
+    _check(st, "graft_accept_sample")
 
 
 def graft_update_adjacency_workspace_size(n_paths, path_stride):

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libgraft.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["graft_api.hip", "tree_build.hip", "tree_attention.hip", "accept.hip",
-           "adjacency.hip", "kv_append.hip"]
+           "adjacency.hip", "kv_append.hip", "accept_sample.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]

@@ -1,0 +1,662 @@
+// Lossless sampling acceptance (temperature T > 0) of the verified hybrid
+// tree, by recursive rejection sampling.
+//
+// Every child of a node proposes its token deterministically; the children
+// are tried in index order against the node's target distribution
+// p = softmax(logits / T).  With residual r (initially p) a proposal of
+// token x is accepted iff u < r(x) = p(x) / (1 - removed mass); on rejection
+// x's mass leaves r, so a repeated token is always rejected.  When no child
+// is accepted the bonus token is drawn from r by inverse CDF over increasing
+// token ids.  The random numbers are inputs (one per child for its test, one
+// per node for its bonus draw).
+//
+// Three launches:
+//  * row_stats_kernel, one workgroup per (node row, vocabulary chunk of two
+//    or eight 16-byte loads per thread): the chunk's max m and its sum of
+//    2^((l - m) log2(e) / T), one float32 exponential per entry, summed
+//    pairwise in float32 within a load and in float64 across loads; the
+//    sum's relative error stays near 1e-6 (the product's rounding in the
+//    exponent dominates), a few ALU operations per entry so that the pass
+//    streams the logits at close to the rate of the greedy argmax.
+//  * sample_walk_kernel, one workgroup per (vocabulary chunk, sequence):
+//    every workgroup of a sequence stages the chunk statistics of all node
+//    rows in LDS, folds them to per-row (max, sum), computes each node's
+//    proposal probability p_parent(token) and walks the tree on one wave
+//    (all of them identically).  Then each workgroup sums the float64
+//    masses of its own chunk of the stop node's row, rejected tokens left
+//    out; the first workgroup writes the accepted path.
+//  * sample_pick_kernel, one workgroup per sequence: a block scan over the
+//    chunk masses finds the chunk that holds rand_sample * total, a block
+//    scan over that chunk's float64 masses finds the token.
+//
+// The bonus token is located among intervals of width p(y), often below
+// 1e-5 of the total for large vocabularies, so its masses are float64 end
+// to end; the acceptance tests compare a random number with one
+// probability, for which the statistics' precision suffices.
+//
+// Method: "Draft Less, Retrieve More" (aitrends.kr summary), architecture
+// paragraph (retrieval nodes are proposals like drafts and verification
+// keeps the target distribution) and the paper's abstract (lossless).
+#include <hip/hip_bf16.h>
+
+#include <climits>
+
+#include "graft_internal.h"
+
+namespace graft {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kLoads = 2;  // 16-byte loads per thread per chunk
+constexpr int kStageLoads = kSampleStage / kThreads;
+template <bool BF16>
+constexpr int per_load() { return BF16 ? 8 : 4; }
+template <bool BF16>
+constexpr int vals() { return kLoads * per_load<BF16>(); }
+template <bool BF16>
+constexpr int chunk_len() { return kThreads * vals<BF16>(); }
+
+// Thread t's values of the L-load chunk starting at lo: element
+// lo + (k * kThreads + t) * per_load + j is v[k * per_load + j], so each
+// load instruction of a wave reads one contiguous kilobyte; entries at or
+// past the vocabulary read as -inf.
+template <bool BF16, bool VEC, int L>
+__device__ inline void load_strided(const void *logits, size_t row, int vocab, int lo,
+                                    float (&v)[L * per_load<BF16>()]) {
+  constexpr int kPer = per_load<BF16>();
+  const int hi = min(vocab, lo + kThreads * L * kPer);
+  if (VEC) {
+    // lo and vocab are multiples of the vector width here
+    const uint4 *x = reinterpret_cast<const uint4 *>(
+        static_cast<const char *>(logits) + row * vocab * (BF16 ? 2 : 4));
+    uint4 raw[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+      const int e = lo + (k * kThreads + (int)threadIdx.x) * kPer;
+      raw[k] = e < hi ? x[e / kPer] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+      const bool in = lo + (k * kThreads + (int)threadIdx.x) * kPer < hi;
+      const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (BF16) {
+          v[k * 8 + 2 * q] = in ? __uint_as_float(w[q] << 16) : -INFINITY;
+          v[k * 8 + 2 * q + 1] = in ? __uint_as_float(w[q] & 0xffff0000u) : -INFINITY;
+        } else {
+          v[k * 4 + q] = in ? __uint_as_float(w[q]) : -INFINITY;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int e = lo + (k * kThreads + (int)threadIdx.x) * kPer + j;
+        float x = -INFINITY;
+        if (e < hi) {
+          if (BF16)
+            x = __uint_as_float((uint32_t)static_cast<const uint16_t *>(logits)[row * vocab + e]
+                                << 16);
+          else
+            x = static_cast<const float *>(logits)[row * vocab + e];
+        }
+        v[k * kPer + j] = x;
+      }
+    }
+  }
+}
+
+// Thread t's values of the chunk starting at lo, contiguous: element
+// lo + t * vals + j is v[j] (two 16-byte loads per thread); entries at or
+// past the vocabulary read as -inf.
+template <bool BF16, bool VEC>
+__device__ inline void load_chunk_contig(const void *logits, size_t row, int vocab, int lo,
+                                         float (&v)[vals<BF16>()]) {
+  constexpr int kPer = per_load<BF16>();
+  constexpr int kV = vals<BF16>();
+  const int hi = min(vocab, lo + chunk_len<BF16>());
+  const int e0 = lo + (int)threadIdx.x * kV;
+  if (VEC) {
+    const uint4 *x = reinterpret_cast<const uint4 *>(
+        static_cast<const char *>(logits) + row * vocab * (BF16 ? 2 : 4));
+    uint4 raw[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int e = e0 + k * kPer;
+      raw[k] = e < hi ? x[e / kPer] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const bool in = e0 + k * kPer < hi;
+      const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (BF16) {
+          v[k * 8 + 2 * q] = in ? __uint_as_float(w[q] << 16) : -INFINITY;
+          v[k * 8 + 2 * q + 1] = in ? __uint_as_float(w[q] & 0xffff0000u) : -INFINITY;
+        } else {
+          v[k * 4 + q] = in ? __uint_as_float(w[q]) : -INFINITY;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int e = e0 + j;
+      float x = -INFINITY;
+      if (e < hi) {
+        if (BF16)
+          x = __uint_as_float((uint32_t)static_cast<const uint16_t *>(logits)[row * vocab + e]
+                              << 16);
+        else
+          x = static_cast<const float *>(logits)[row * vocab + e];
+      }
+      v[j] = x;
+    }
+  }
+}
+
+// 2^x in float64 for x <= 0, without branches: x = n + f with n = rint(x)
+// and |f| <= 1/2, 2^f = e^(f ln 2) by its Taylor series to degree 13
+// (truncation below 5e-18 relative), then scaled by 2^n.  Arguments below
+// -1100 (and -inf) give 0.
+struct Exp2Coeffs {
+  double c[14];
+  constexpr Exp2Coeffs() : c() {
+    const double ln2 = 0.69314718055994530942;
+    double t = 1.0;
+    for (int i = 0; i < 14; ++i) {
+      c[i] = t;
+      t = t * ln2 / (i + 1);
+    }
+  }
+};
+constexpr Exp2Coeffs kExp2{};
+__device__ inline double exp2_nonpos(double x) {
+  x = fmax(x, -1100.0);
+  const double n = __builtin_rint(x);
+  const double f = x - n;
+  double p = kExp2.c[13];
+#pragma unroll
+  for (int i = 12; i >= 0; --i) p = fma(p, f, kExp2.c[i]);
+  return __builtin_ldexp(p, (int)n);
+}
+
+// Bit j: this thread's contiguous value j of the chunk starting at lo is
+// one of the n tokens in gone[].
+template <bool BF16>
+__device__ inline uint32_t gone_bits_contig(const int32_t *gone, int n, int lo) {
+  constexpr int kV = vals<BF16>();
+  uint32_t bits = 0;
+  for (int g = 0; g < n; ++g) {
+    const int off = gone[g] - lo;
+    if (off >= 0 && off < chunk_len<BF16>() && off / kV == (int)threadIdx.x)
+      bits |= 1u << (off % kV);
+  }
+  return bits;
+}
+
+__device__ inline float logit_at(const void *logits, bool bf16, size_t idx) {
+  if (bf16) return __uint_as_float((uint32_t)static_cast<const uint16_t *>(logits)[idx] << 16);
+  return static_cast<const float *>(logits)[idx];
+}
+
+__device__ inline float wave_max_f(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline double wave_sum_d(double x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Block-wide sum in a fixed order; every thread gets the total.
+__device__ inline double block_sum_d(double x, double *red) {
+  x = wave_sum_d(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Block-wide scan in thread order.  Returns the inclusive prefix; *excl gets
+// the exclusive one and *total the block total.  Thread t's exclusive prefix
+// is bit-identical to thread t-1's inclusive one and the last thread's
+// inclusive prefix to the total, so the intervals [excl, incl) tile
+// [0, total) without gaps or overlaps.
+__device__ inline double block_scan_d(double x, double *red, double *excl, double *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  double prev = __shfl_up(x, 1);
+  if (lane == 0) prev = 0.0;
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  double before = 0.0, t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) before += red[w];
+    t += red[w];
+  }
+  __syncthreads();
+  *total = t;
+  *excl = lane == 0 ? before : before + prev;
+  return before + x;
+}
+
+// float64 mass of a logit of a row whose max is row_max (0 for -inf).
+__device__ inline double mass64(float l, float row_max, double k) {
+  return exp2_nonpos(((double)l - (double)row_max) * k);
+}
+
+// float32 2^(d k) for d <= 0 (-inf included) with the exponent's product
+// rounding corrected to first order (k = k_hi + k_lo); relative error near
+// 1.2e-7.  Exponents below -160 give 0 (the select also discards the
+// non-finite corrections of huge products).
+__device__ inline float exp2_split(float d, float k_hi, float k_lo) {
+  constexpr float kLn2f = 0.69314718055994531f;
+  const float xh = d * k_hi;
+  const float xl = fmaf(d, k_hi, -xh) + d * k_lo;
+  const float e = __builtin_amdgcn_exp2f(xh);
+  const float r = fmaf(e, xl * kLn2f, e);
+  return xh > -160.f ? r : 0.f;
+}
+
+// ------------------------------------------------------------ row statistics
+template <bool BF16, bool VEC, int L>
+__global__ __launch_bounds__(kThreads) void row_stats_kernel(SampleParams p) {
+  constexpr int kPer = per_load<BF16>();
+  constexpr int kV = L * kPer;
+  const int c = blockIdx.x;
+  const int row = blockIdx.y;
+  const int b = row / p.n_max, i = row % p.n_max;
+  if (i >= max(p.n_nodes[b], 1)) return;  // rows past the tree are not read
+  float v[kV];
+  load_strided<BF16, VEC, L>(p.logits, (size_t)row, p.vocab, c * kThreads * kV, v);
+  __shared__ float red[kWaves];
+  __shared__ double zred[kWaves];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kV; ++k) m = fmaxf(m, v[k]);
+  m = wave_max_f(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // each load's values summed pairwise in float32 (three roundings at
+  // most), the loads' sums in float64
+  double z = 0.0;
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    float e[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) e[j] = __builtin_amdgcn_exp2f((v[k * kPer + j] - m) * p.k_hi);
+#pragma unroll
+    for (int w = kPer / 2; w > 0; w >>= 1)
+#pragma unroll
+      for (int j = 0; j < w; ++j) e[j] += e[j + w];
+    z += (double)e[0];
+  }
+  z = wave_sum_d(z);
+  if ((threadIdx.x & 63) == 0) zred[threadIdx.x >> 6] = z;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ChunkStat st;
+    st.m = m;
+    st.pad = 0.f;
+    st.z = m > -INFINITY ? ((zred[0] + zred[1]) + zred[2]) + zred[3] : 0.0;
+    p.stats[(size_t)row * p.chunks + c] = st;
+  }
+}
+
+// ------------------------------------------------------------------ the walk
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_walk_kernel(SampleParams p) {
+  constexpr int kVals = vals<BF16>();
+  constexpr int kChunk = chunk_len<BF16>();
+  const int c_own = blockIdx.x;  // this workgroup's chunk of the stop row
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ ChunkStat s_stage[kSampleStage];
+  __shared__ float s_m[GRAFT_MAX_NODES];      // row max
+  __shared__ double s_z[GRAFT_MAX_NODES];     // row sum of 2^((l - max) k)
+  __shared__ int32_t s_parent[GRAFT_MAX_NODES];
+  __shared__ int32_t s_token[GRAFT_MAX_NODES];
+  __shared__ double s_prob[GRAFT_MAX_NODES];  // p_parent(token) of each node
+  __shared__ float s_u[GRAFT_MAX_NODES];
+  __shared__ int32_t s_path[GRAFT_MAX_NODES];
+  __shared__ int32_t s_gone[GRAFT_MAX_NODES];  // tokens rejected at the stop node
+  __shared__ double s_red[kWaves];
+  __shared__ int s_len, s_ngone, s_stop;
+
+  const size_t base_row = (size_t)b * p.n_max;
+  // ---- tree arrays, random numbers and node count (one round of loads)
+  const int nn = p.n_nodes[b];
+  int par = -1, tok = -1;
+  float u = 0.f;
+  if (tid < p.n_max) {
+    par = p.tree_parent[base_row + tid];
+    tok = p.tree_token[base_row + tid];
+    u = p.rand_accept[base_row + tid];
+  }
+  const int n = min(max(nn, 1), p.n_max);
+  if (tid >= n) par = tok = -1;
+  if (par >= tid) par = -1;
+  if (tid < p.n_max) {
+    s_parent[tid] = par;
+    s_token[tid] = tok;
+    s_u[tid] = u;
+    s_prob[tid] = 0.0;
+  }
+  // ---- the proposal's logit under its parent's row (issued before the
+  // statistics are staged)
+  const bool has_logit = tid > 0 && par >= 0 && tok >= 0 && tok < p.vocab;
+  const float l_prop =
+      has_logit ? logit_at(p.logits, BF16, (base_row + par) * p.vocab + tok) : 0.f;
+
+  // ---- fold the chunk statistics of every row: stage a group of rows in
+  // LDS with all loads issued at once, then Q threads per row
+  const int chunks = p.chunks;
+  const int rows_per_group = max(1, kSampleStage / chunks);
+  for (int r0 = 0; r0 < n; r0 += rows_per_group) {
+    const int R = min(rows_per_group, n - r0);
+    const int ents = R * chunks;
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.stats + (base_row + r0) * chunks);
+    uint4 tmp[kStageLoads];
+#pragma unroll
+    for (int k = 0; k < kStageLoads; ++k) {
+      const int e = k * kThreads + tid;
+      tmp[k] = e < ents ? src[e] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < kStageLoads; ++k) {
+      const int e = k * kThreads + tid;
+      if (e < ents) reinterpret_cast<uint4 *>(s_stage)[e] = tmp[k];
+    }
+    __syncthreads();
+    int Q = 1;
+    while (Q < 64 && Q * 2 * R <= kThreads) Q *= 2;
+    const int ri = tid / Q, q = tid % Q;
+    float m = -INFINITY;
+    if (ri < R)
+      for (int c = q; c < chunks; c += Q) {
+        const ChunkStat st = s_stage[ri * chunks + c];
+        if (st.z > 0.0) m = fmaxf(m, st.m);
+      }
+    for (int o = 1; o < Q; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    double z = 0.0;
+    if (ri < R && m > -INFINITY)
+      for (int c = q; c < chunks; c += Q) {
+        const ChunkStat st = s_stage[ri * chunks + c];
+        z = fma(st.z, (double)exp2_split(st.m - m, p.k_hi, p.k_lo), z);
+      }
+    for (int o = 1; o < Q; o <<= 1) z += __shfl_xor(z, o);
+    if (ri < R && q == 0) {
+      s_m[r0 + ri] = m;
+      s_z[r0 + ri] = z;
+    }
+    __syncthreads();  // the next group overwrites the staging area
+  }
+  // ---- proposal probability of every node under its parent's distribution
+  if (has_logit && s_z[par] > 0.0) s_prob[tid] = mass64(l_prop, s_m[par], p.k_log2) / s_z[par];
+  __syncthreads();
+
+  // ---- the walk (wave 0): children of the current node in index order
+  if (wave == 0) {
+    int node = 0, len = 1, ngone = 0;
+    int gone_lo = INT_MIN, gone_hi = INT_MIN;  // lane g holds rejected token g / g + 64
+    while (true) {
+      double removed = 0.0;
+      ngone = 0;
+      gone_lo = gone_hi = INT_MIN;
+      int next = -1;
+      for (int base = node + 1; base < n && next < 0; base += 64) {
+        const int c = base + lane;
+        unsigned long long bal = __ballot(c < n && s_parent[c] == node);
+        while (bal) {
+          const int cc = base + __builtin_ctzll(bal);  // uniform
+          bal &= bal - 1;
+          const int x = s_token[cc];
+          if (__ballot(gone_lo == x || gone_hi == x)) continue;  // mass already gone
+          // u < p(x) / (1 - removed), without the division
+          if ((double)s_u[cc] * (1.0 - removed) < s_prob[cc]) {
+            next = cc;
+            break;
+          }
+          if (ngone < 64) {
+            if (lane == ngone) gone_lo = x;
+          } else if (lane == ngone - 64) {
+            gone_hi = x;
+          }
+          ++ngone;
+          removed += s_prob[cc];
+        }
+      }
+      if (next < 0) break;
+      node = next;
+      if (lane == 0) s_path[len] = node;
+      ++len;
+    }
+    if (lane == 0) {
+      s_path[0] = 0;
+      s_len = len;
+      s_ngone = ngone;
+      s_stop = node;
+    }
+    if (lane < ngone) s_gone[lane] = gone_lo;
+    if (lane + 64 < ngone) s_gone[lane + 64] = gone_hi;
+  }
+  __syncthreads();
+
+  // ---- this workgroup's chunk of the stop row: float64 residual mass
+  const int s = s_stop, ng = s_ngone, len = s_len;
+  const size_t srow = base_row + s;
+  const float row_max = s_m[s];
+  {
+    float v[kVals];
+    load_chunk_contig<BF16, VEC>(p.logits, srow, p.vocab, c_own * kChunk, v);
+    const uint32_t bits = gone_bits_contig<BF16>(s_gone, ng, c_own * kChunk);
+    const float mref = row_max > -INFINITY ? row_max : 0.f;  // -inf row: no mass
+    double mk[kVals];
+#pragma unroll
+    for (int k = 0; k < kVals; ++k)
+      mk[k] = mass64(v[k], mref, p.k_log2) * (double)(1u - ((bits >> k) & 1u));
+    double part = 0.0;
+#pragma unroll
+    for (int k = 0; k < kVals; ++k) part += mk[k];
+    const double tot = block_sum_d(part, s_red);
+    if (tid == 0) p.chunk_w[(size_t)b * p.wchunks + c_own] = tot;
+  }
+  if (c_own != 0) return;
+
+  // ---- the accepted path (the bonus token is written by the pick kernel)
+  int32_t *pn = p.path_nodes + base_row;
+  int32_t *pt = p.path_tokens + (size_t)b * (p.n_max + 1);
+  for (int k = tid; k < p.n_max + 1; k += kThreads) {
+    if (k < p.n_max) pn[k] = k < len ? s_path[k] : -1;
+    if (k != len) pt[k] = k < len ? s_token[s_path[k]] : -1;
+  }
+  SampleRec *rec = p.rec + b;
+  if (tid < ng) rec->gone[tid] = s_gone[tid];
+  if (tid == 0) {
+    p.accept_len[b] = len - 1;
+    rec->stop = s;
+    rec->len = len;
+    rec->ngone = ng;
+    rec->row_max = row_max;
+    rec->u = p.rand_sample[srow];
+  }
+}
+
+// ------------------------------------------------------------ the bonus draw
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleParams p) {
+  constexpr int kVals = vals<BF16>();
+  constexpr int kChunk = chunk_len<BF16>();
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ int32_t s_gone[GRAFT_MAX_NODES];
+  __shared__ double s_red[kWaves];
+  __shared__ int s_cstar, s_clast, s_bonus, s_elast;
+  __shared__ double s_tin;
+
+  const SampleRec *rec = p.rec + b;
+  const int chunks = p.wchunks;
+  const double *w_row = p.chunk_w + (size_t)b * chunks;
+  // one round: the record and the first group of chunk masses
+  const int s = rec->stop, len = rec->len, ng = rec->ngone;
+  const float row_max = rec->row_max;
+  const float u = rec->u;
+  const double w0 = tid < chunks ? w_row[tid] : 0.0;
+  if (tid < ng) s_gone[tid] = rec->gone[tid];
+  if (tid == 0) {
+    s_cstar = -1;
+    s_clast = -1;
+    s_bonus = -1;
+    s_elast = -1;
+  }
+  // total residual mass, then the chunk holding the target.  With at most
+  // one chunk per thread a single scan gives both; otherwise the same scan
+  // runs twice, so that the final carry equals the total bit for bit.
+  double total = 0.0, incl0 = 0.0, ex0 = 0.0;
+  for (int c0 = 0; c0 < chunks; c0 += kThreads) {
+    const int c = c0 + tid;
+    const double w = c0 == 0 ? w0 : (c < chunks ? w_row[c] : 0.0);
+    double ex, gt;
+    const double incl = block_scan_d(w, s_red, &ex, &gt);
+    if (c0 == 0) {
+      incl0 = incl;
+      ex0 = ex;
+    }
+    total += gt;
+  }
+  const double target = (double)u * total;
+  double carry = 0.0;
+  for (int c0 = 0; c0 < chunks; c0 += kThreads) {
+    const int c = c0 + tid;
+    const double w = c0 == 0 ? w0 : (c < chunks ? w_row[c] : 0.0);
+    double ex = ex0, incl = incl0, gt = total;
+    if (chunks > kThreads) incl = block_scan_d(w, s_red, &ex, &gt);
+    const double lo = carry + ex, hi = carry + incl;
+    if (w > 0.0) {
+      atomicMax(&s_clast, c);
+      if (target >= lo && target < hi) {
+        s_cstar = c;
+        s_tin = target - lo;
+      }
+    }
+    carry += gt;
+  }
+  __syncthreads();
+  int cstar = s_cstar;
+  double tin = s_tin;
+  if (cstar < 0) {
+    // total 0 (every token rejected), or rounding put the target at the top
+    cstar = s_clast;
+    tin = cstar >= 0 ? w_row[cstar] : 0.0;
+  }
+  if (cstar >= 0) {
+    // the chunk's float64 masses, each thread a contiguous run of entries
+    const size_t srow = (size_t)b * p.n_max + s;
+    const int lo_e = cstar * kChunk;
+    float v[kVals];
+    load_chunk_contig<BF16, VEC>(p.logits, srow, p.vocab, lo_e, v);
+    const uint32_t bits = gone_bits_contig<BF16>(s_gone, ng, lo_e);
+    // a row of -inf logits has no mass: compare against -inf as a max of 0
+    const float mref = row_max > -INFINITY ? row_max : 0.f;
+    double mass[kVals];
+    double gs = 0.0;
+    int jlast = -1;
+#pragma unroll
+    for (int k = 0; k < kVals; ++k)
+      mass[k] = mass64(v[k], mref, p.k_log2) * (double)(1u - ((bits >> k) & 1u));
+#pragma unroll
+    for (int k = 0; k < kVals; ++k) {
+      gs += mass[k];
+      if (mass[k] > 0.0) jlast = k;
+    }
+    const int e0 = lo_e + tid * kVals;
+    if (jlast >= 0) atomicMax(&s_elast, e0 + jlast);
+    double ex, gt;
+    const double incl = block_scan_d(gs, s_red, &ex, &gt);
+    if (gs > 0.0 && tin >= ex && tin < incl) {
+      double acc = ex;
+      int pick = jlast;
+#pragma unroll
+      for (int k = 0; k < kVals; ++k) {
+        acc += mass[k];
+        if (acc > tin && mass[k] > 0.0) {
+          pick = k;
+          break;
+        }
+      }
+      s_bonus = e0 + pick;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int y = s_bonus;
+    if (y < 0) y = s_elast >= 0 ? s_elast : p.vocab - 1;
+    p.path_tokens[(size_t)b * (p.n_max + 1) + len] = y;
+  }
+}
+
+// 16-byte loads per thread of a statistics chunk: 2 (4096 bf16 / 2048 f32
+// entries) while the grid is small, 8 once it would exceed 8192 workgroups,
+// where fewer and larger workgroups stream faster.
+constexpr int kStatSmall = 2, kStatLarge = 8, kStatLargeGrid = 8192;
+int stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab) {
+  const long long small = (vocab + (long long)kThreads * kStatSmall * (dtype == GRAFT_BF16 ? 8 : 4) - 1) /
+                          ((long long)kThreads * kStatSmall * (dtype == GRAFT_BF16 ? 8 : 4));
+  return (long long)rows * small > kStatLargeGrid ? kStatLarge : kStatSmall;
+}
+
+template <bool BF16, bool VEC>
+void launch(const SampleParams &p, hipStream_t stream) {
+  if (p.stat_loads == kStatLarge)
+    hipLaunchKernelGGL((row_stats_kernel<BF16, VEC, kStatLarge>), dim3(p.chunks, p.batch * p.n_max),
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((row_stats_kernel<BF16, VEC, kStatSmall>), dim3(p.chunks, p.batch * p.n_max),
+                       dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((sample_walk_kernel<BF16, VEC>), dim3(p.wchunks, p.batch), dim3(kThreads),
+                     0, stream, p);
+  hipLaunchKernelGGL((sample_pick_kernel<BF16, VEC>), dim3(p.batch), dim3(kThreads), 0, stream,
+                     p);
+}
+
+}  // namespace
+
+int32_t sample_stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab) {
+  return stat_loads(dtype, rows, vocab);
+}
+
+int32_t sample_stat_chunks(graft_dtype dtype, int32_t loads, int32_t vocab) {
+  const long long len = (long long)kThreads * loads * (dtype == GRAFT_BF16 ? 8 : 4);
+  return (int32_t)((vocab + len - 1) / len);
+}
+
+int32_t sample_walk_chunks(graft_dtype dtype, int32_t vocab) {
+  const int len = dtype == GRAFT_BF16 ? chunk_len<true>() : chunk_len<false>();
+  return (vocab + len - 1) / len;
+}
+
+void launch_accept_sample(graft_dtype dtype, const SampleParams &p, hipStream_t stream) {
+  if (dtype == GRAFT_BF16) {
+    if (p.vocab % 8 == 0) launch<true, true>(p, stream);
+    else launch<true, false>(p, stream);
+  } else {
+    if (p.vocab % 4 == 0) launch<false, true>(p, stream);
+    else launch<false, false>(p, stream);
+  }
+}
+
+}  // namespace graft

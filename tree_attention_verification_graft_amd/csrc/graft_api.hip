@@ -29,6 +29,17 @@ graft_status check_launch(const char *what) {
   return GRAFT_OK;
 }
 
+SampleLayout sample_layout(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab) {
+  // statistics sized for the smaller chunks (the most per row)
+  const size_t chunks = (size_t)sample_stat_chunks(dtype, 2, vocab);
+  const size_t wchunks = (size_t)sample_walk_chunks(dtype, vocab);
+  SampleLayout l{};
+  l.off_chunk_w = align_up((size_t)batch * n_max * chunks * sizeof(ChunkStat), 256);
+  l.off_rec = l.off_chunk_w + align_up((size_t)batch * wchunks * sizeof(double), 256);
+  l.total = l.off_rec + align_up((size_t)batch * sizeof(SampleRec), 256);
+  return l;
+}
+
 }  // namespace graft
 
 using namespace graft;
@@ -276,6 +287,71 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32
   p.partial = static_cast<unsigned long long *>(workspace);
   launch_accept(dtype, p, stream);
   return check_launch("graft_accept");
+}
+
+// ------------------------------------------------------ sampling acceptance
+size_t graft_accept_sample_workspace_size(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                          int32_t vocab) {
+  if ((dtype != GRAFT_F32 && dtype != GRAFT_BF16) || batch < 0 || n_max < 1 ||
+      n_max > GRAFT_MAX_NODES || vocab < 1)
+    return 0;
+  return sample_layout(dtype, batch, n_max, vocab).total;
+}
+
+graft_status graft_accept_sample(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab,
+                                 const void *logits, float temperature,
+                                 const int32_t *tree_token, const int32_t *tree_parent,
+                                 const int32_t *n_nodes, const float *rand_accept,
+                                 const float *rand_sample, int32_t *accept_len,
+                                 int32_t *path_nodes, int32_t *path_tokens, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(dtype == GRAFT_F32 || dtype == GRAFT_BF16, GRAFT_ERR_INVALID_ARG,
+          "graft_accept_sample: unknown dtype %d", (int)dtype);
+  REQUIRE(batch >= 0 && batch <= 65535 && n_max >= 1 && n_max <= GRAFT_MAX_NODES,
+          GRAFT_ERR_INVALID_ARG, "graft_accept_sample: batch/n_max out of range");
+  REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_accept_sample: vocab < 1");
+  REQUIRE(std::isfinite(temperature) && temperature > 0.f, GRAFT_ERR_INVALID_ARG,
+          "graft_accept_sample: temperature must be finite and > 0");
+  const double k_log2 = 1.4426950408889634 / (double)temperature;
+  REQUIRE(k_log2 < 1e37, GRAFT_ERR_UNSUPPORTED, "graft_accept_sample: temperature below 1e-37");
+  REQUIRE((long long)batch * n_max <= 65535, GRAFT_ERR_UNSUPPORTED,
+          "graft_accept_sample: batch * n_max above 65535");
+  REQUIRE(sample_stat_chunks(dtype, 2, vocab) <= kSampleStage, GRAFT_ERR_UNSUPPORTED,
+          "graft_accept_sample: vocab above %d", kSampleStage * (dtype == GRAFT_BF16 ? 4096 : 2048));
+  if (batch == 0) return GRAFT_OK;
+  REQUIRE(logits && tree_token && tree_parent && n_nodes && rand_accept && rand_sample &&
+              accept_len && path_nodes && path_tokens,
+          GRAFT_ERR_INVALID_ARG, "graft_accept_sample: null device pointer");
+  const size_t need = graft_accept_sample_workspace_size(dtype, batch, n_max, vocab);
+  REQUIRE(workspace && workspace_bytes >= need, GRAFT_ERR_WORKSPACE,
+          "graft_accept_sample: workspace of %zu bytes needed, %zu given", need,
+          workspace_bytes);
+  SampleParams p{};
+  p.batch = batch;
+  p.n_max = n_max;
+  p.vocab = vocab;
+  p.stat_loads = sample_stat_loads(dtype, batch * n_max, vocab);
+  p.chunks = sample_stat_chunks(dtype, p.stat_loads, vocab);
+  p.wchunks = sample_walk_chunks(dtype, vocab);
+  p.k_log2 = k_log2;
+  p.k_hi = (float)k_log2;
+  p.k_lo = (float)(k_log2 - (double)p.k_hi);
+  p.logits = logits;
+  p.tree_token = tree_token;
+  p.tree_parent = tree_parent;
+  p.n_nodes = n_nodes;
+  p.rand_accept = rand_accept;
+  p.rand_sample = rand_sample;
+  p.accept_len = accept_len;
+  p.path_nodes = path_nodes;
+  p.path_tokens = path_tokens;
+  const SampleLayout lay = sample_layout(dtype, batch, n_max, vocab);
+  p.stats = static_cast<ChunkStat *>(workspace);
+  p.chunk_w = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.off_chunk_w);
+  p.rec = reinterpret_cast<SampleRec *>(static_cast<char *>(workspace) + lay.off_rec);
+  launch_accept_sample(dtype, p, stream);
+  return check_launch("graft_accept_sample");
 }
 
 // ---------------------------------------------------------------- adjacency

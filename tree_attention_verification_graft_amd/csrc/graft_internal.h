@@ -118,6 +118,52 @@ void launch_tree_pairs(int32_t batch, int32_t n_max, const int32_t *tree_token,
                        const int32_t *argmax, const int32_t *n_nodes, int32_t *pairs,
                        int32_t *lens, hipStream_t stream);
 
+// ------------------------------------------------------ sampling acceptance
+struct ChunkStat {
+  float m;    // chunk max
+  float pad;
+  double z;   // chunk sum of exp2((l - m) * log2(e) / temperature)
+};
+// What the walk hands to the bonus draw, per sequence.
+struct alignas(16) SampleRec {
+  int32_t stop, len, ngone, pad;
+  float row_max;  // max logit of the stop node's row
+  float u;        // rand_sample of the stop node
+  int32_t pad2[2];
+  int32_t gone[GRAFT_MAX_NODES];  // tokens rejected at the stop node
+};
+constexpr int kSampleStage = 2304;  // chunk records one workgroup stages in LDS (36 KB)
+struct SampleParams {
+  int32_t batch, n_max, vocab;
+  int32_t chunks, stat_loads;  // statistics chunks per row, loads per thread of one
+  int32_t wchunks;             // chunks of the stop row's float64 masses
+  double k_log2;   // log2(e) / temperature
+  float k_hi, k_lo;  // k_log2 split into a float and the float of the rest
+  const void *logits;
+  const int32_t *tree_token;
+  const int32_t *tree_parent;
+  const int32_t *n_nodes;
+  const float *rand_accept;
+  const float *rand_sample;
+  int32_t *accept_len;
+  int32_t *path_nodes;
+  int32_t *path_tokens;
+  ChunkStat *stats;  // [batch * n_max][chunks]
+  double *chunk_w;   // [batch][wchunks] residual mass of the stop row per chunk
+  SampleRec *rec;    // [batch]
+};
+// Statistics chunks: loads per thread for a launch over `rows` node rows,
+// and chunks per row at that many loads (2048 or 1024 entries per load).
+int32_t sample_stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab);
+int32_t sample_stat_chunks(graft_dtype dtype, int32_t loads, int32_t vocab);
+// Chunks of the stop row's float64 masses (4096 bf16 or 2048 f32 entries).
+int32_t sample_walk_chunks(graft_dtype dtype, int32_t vocab);
+struct SampleLayout {
+  size_t off_chunk_w, off_rec, total;
+};
+SampleLayout sample_layout(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab);
+void launch_accept_sample(graft_dtype dtype, const SampleParams &p, hipStream_t stream);
+
 // ------------------------------------------------------------ KV append
 struct AppendParams {
   int32_t batch, n_max, hkv, head_dim, block_size, max_blocks, num_blocks;

@@ -77,6 +77,11 @@ class DeviceStep:
         self.attn_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=d)
         n = G.graft_accept_workspace_size(B, self.n_max, w.V)
         self.accept_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=d)
+        n = G.graft_accept_sample_workspace_size(w.dtype, B, self.n_max, w.V)
+        self.sample_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=d)
+        # the random numbers of sampling acceptance (set by the caller)
+        self.rand_accept = torch.zeros((B, self.n_max), dtype=torch.float32, device=d)
+        self.rand_sample = torch.zeros((B, self.n_max), dtype=torch.float32, device=d)
         n = G.graft_update_adjacency_workspace_size(B, self.n_max + 1)
         if alloc_update_for_prompt and w.prompt is not None:
             n = max(n, G.graft_update_adjacency_workspace_size(1, len(w.prompt)))
@@ -101,6 +106,14 @@ class DeviceStep:
         G.graft_accept(self.logits, self.tree_token, self.tree_parent, self.tree_mask,
                        self.n_nodes, self.argmax, self.accept_len, self.path_nodes,
                        self.path_tokens, self.accept_ws)
+
+    def accept_sample(self, temperature: float):
+        """Sampling acceptance at `temperature` > 0 in place of the greedy
+        one, with the random numbers in rand_accept / rand_sample."""
+        G.graft_accept_sample(self.logits, temperature, self.tree_token, self.tree_parent,
+                              self.n_nodes, self.rand_accept, self.rand_sample,
+                              self.accept_len, self.path_nodes, self.path_tokens,
+                              self.sample_ws)
 
     def update(self):
         G.graft_update_adjacency(self.m_ids, self.m_scores, self.path_tokens, self.accept_len,

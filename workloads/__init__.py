@@ -2,5 +2,5 @@
 and the benchmark.  Holds no part of the method's arithmetic."""
 from .synth import (  # noqa: F401
     CONFIG_ORDER, PRESETS, STAGE_DEPTHS, TAU, Workload, Zipf, envelope,
-    f32_to_bf16_bits, make, make_from_spec, plant_path,
+    f32_to_bf16_bits, make, make_from_spec, plant_path, sampling_uniforms,
 )

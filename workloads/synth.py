@@ -354,12 +354,13 @@ def make_from_spec(name: str, spec: dict) -> Workload:
 # ----------------------------------------------------------------------------
 
 def plant_path(logits: np.ndarray, dtype: str, tree_token, tree_parent,
-               n_nodes, seed: int) -> np.ndarray:
+               n_nodes, seed: int, boost: float = 1.0) -> np.ndarray:
     """Return a copy of logits in which, for each sequence, a seeded target
     node t is made acceptable: for every edge p -> c on the root path of t,
-    row p's entry at token(c) becomes its row maximum plus one.  Random
+    row p's entry at token(c) becomes its row maximum plus `boost`.  Random
     logits alone would accept almost nothing; this plants a path of length
-    depth(t) without touching how acceptance is decided."""
+    depth(t) without touching how acceptance is decided (under sampling, a
+    larger boost makes the planted tokens likely rather than certain)."""
     out = logits.copy()
     rng = np.random.default_rng(seed)
     B = out.shape[0]
@@ -374,9 +375,19 @@ def plant_path(logits: np.ndarray, dtype: str, tree_token, tree_parent,
             tok = int(tree_token[b, c])
             if dtype == "bf16":
                 row = (out[b, p].astype(np.uint32) << np.uint32(16)).view(np.float32)
-                top = np.float32(row.max()) + np.float32(1.0)
+                top = np.float32(row.max()) + np.float32(boost)
                 out[b, p, tok] = f32_to_bf16_bits(np.array([top], np.float32))[0]
             else:
-                out[b, p, tok] = np.float32(out[b, p].max()) + np.float32(1.0)
+                out[b, p, tok] = np.float32(out[b, p].max()) + np.float32(boost)
             c = p
     return out
+
+
+def sampling_uniforms(seed: int, batch: int, n_max: int):
+    """The random numbers of sampling acceptance, as float32 in [0, 1):
+    rand_accept[b][i] (child i's test) and rand_sample[b][i] (node i's bonus
+    draw)."""
+    rng = np.random.default_rng(seed)
+    ra = rng.random((batch, n_max), dtype=np.float32)
+    rs = rng.random((batch, n_max), dtype=np.float32)
+    return ra, rs
