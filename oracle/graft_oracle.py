@@ -30,7 +30,8 @@ that implements it; the full list of readings lives with the design notes.
 
 O5 (append_kv) commits the accepted path to the KV cache, the step that
 follows verification when decoding continues; O6 (accept_sample) is the
-temperature > 0 acceptance.
+temperature > 0 acceptance; O7 (rope, tree_attention_rope, append_kv_rope)
+rotates queries and keys by their tree positions inside those two steps.
 
 Conventions shared with the C header (by specification, not by code):
   * draft arrays  [B][n_draft_max]: parent (-1 = child of the root; otherwise
@@ -311,6 +312,66 @@ def tree_attention(q, k_tree, v_tree, k_cache, v_cache, block_table,
             w = np.exp(s - s.max())
             out[b, i, hq, :] = (w @ V) / w.sum()
     return out
+
+
+# ----------------------------------------------------------------------------
+# O7: rotary position embedding by tree position, fused into the verification
+# attention and the commit ([AT-arch] one target forward with tree attention;
+# positions prefix + depth, reading D13).  The pages do not name the target's
+# positional scheme; the workloads' targets (Llama 3, Qwen3) use rotary
+# embeddings (RoFormer, Su et al. 2021) with the "rotate half" pairing of dim
+# i with dim i + D/2.  The caller supplies the table of cosines and sines.
+# ----------------------------------------------------------------------------
+
+def rope(x, pos, cos_sin):
+    """Rotate the last axis of x (float64, even length D) by positions pos.
+
+    cos_sin is the caller's table [positions][D]: row t holds cos(t w_i) in
+    its first D/2 entries and sin(t w_i) in the last D/2.  For i < D/2 the
+    pair (x_i, x_{i+D/2}) becomes (x_i c - x_{i+D/2} s, x_{i+D/2} c + x_i s)
+    with (c, s) from row pos.  pos broadcasts against x's leading axes."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    tab = np.asarray(cos_sin, dtype=np.float64)[np.asarray(pos)]
+    c, s = tab[..., :h], tab[..., h:]
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def tree_attention_rope(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+                        tree_mask, n_nodes, tree_pos, cos_sin, scale, rows=None):
+    """Tree attention whose queries and tree keys arrive unrotated: node i's
+    query and key are rotated by its position tree_pos[b][i] first; the
+    cached prefix keys were rotated when they were written.  Then exactly
+    `tree_attention`.  All arrays float64 (bf16 widened exactly)."""
+    pos = np.asarray(tree_pos)[:, :, None]  # broadcast over heads
+    qr = rope(q, pos, cos_sin)
+    kr = rope(k_tree, pos, cos_sin)
+    return tree_attention(qr, kr, v_tree, k_cache, v_cache, block_table, prefix_len,
+                          tree_mask, n_nodes, scale, rows=rows)
+
+
+def append_kv_rope(k_cache, v_cache, block_table, prefix_len, k_tree, v_tree,
+                   path_nodes, accept_len, cos_sin):
+    """`append_kv` for unrotated tree keys: the committed key of cache token
+    t = prefix_len + j is rope(k_tree[node], t); values are copied.
+
+    k_cache, k_tree float64 (bf16 widened exactly); v arrays of any dtype.
+    Returns (k float64 with the committed rows exact, v, new prefix_len)."""
+    k, v, new_len = append_kv(k_cache, v_cache, block_table, prefix_len, k_tree, v_tree,
+                              path_nodes, accept_len)
+    k = np.asarray(k, dtype=np.float64)
+    blk = k.shape[2]
+    for b in range(len(prefix_len)):
+        L = int(accept_len[b])
+        P = int(prefix_len[b])
+        for j in range(L + 1):
+            node = int(path_nodes[b][j])
+            t = P + j
+            page = int(block_table[b][t // blk])
+            k[page, :, t % blk, :] = rope(k_tree[b, node, :, :], t, cos_sin)
+    return k, v, new_len
 
 
 # ----------------------------------------------------------------------------

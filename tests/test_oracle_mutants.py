@@ -14,6 +14,7 @@ import pytest
 import oracle.graft_oracle as real
 import test_oracle_accept_update as T_au
 import test_oracle_append as T_ap
+import test_oracle_rope as T_ro
 import test_oracle_sample as T_sa
 import test_oracle_update_tree as T_ut
 import test_oracle_attention as T_at
@@ -43,8 +44,8 @@ MUTANTS = [
     ("update ties by id desc", "key=lambda kv: (-kv[1], kv[0]))[:S]", "key=lambda kv: (-kv[1], -kv[0]))[:S]"),
     ("update forgets old score", "cand[v] = cand.get(v, 0.0) + float(c)", "cand[v] = float(c)"),
     ("bonus transition dropped", "for k in range(L + 1):", "for k in range(L):"),
-    ("commit one slot late", "            t = P + j\n", "            t = P + j + 1\n"),
-    ("commit drops the deepest node", "        for j in range(L + 1):\n            node", "        for j in range(L):\n            node"),
+    ("commit one slot late", "            t = P + j\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree", "            t = P + j + 1\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree"),
+    ("commit drops the deepest node", "        for j in range(L + 1):\n            node = int(path_nodes[b][j])\n            t = P + j\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree", "        for j in range(L):\n            node = int(path_nodes[b][j])\n            t = P + j\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree"),
     ("commit length short", "new_len[b] = P + L + 1", "new_len[b] = P + L"),
     ("commit V from K", "v[page, :, :, t % blk] = v_tree[b, node, :, :]", "v[page, :, :, t % blk] = k_tree[b, node, :, :]"),
     ("tree update skips the root", "        for i in range(int(n_nodes[b])):\n            pairs.append", "        for i in range(1, int(n_nodes[b])):\n            pairs.append"),
@@ -53,6 +54,11 @@ MUTANTS = [
     ("bonus keeps rejected mass", "                    r[x] = 0.0\n", "                    r[x] = r[x]\n"),
     ("sampling accepts on u > r(x)", "                if u < thr:\n", "                if u > thr:\n"),
     ("bonus from the root's row", "                r = p.copy()\n", "                r = np.exp(lg[b, 0] / T - (lg[b, 0] / T).max()); r /= r.sum()\n"),
+    ("rope sine sign flipped", "[x1 * c - x2 * s, x2 * c + x1 * s]", "[x1 * c + x2 * s, x2 * c - x1 * s]"),
+    ("rope pairs adjacent dims", "    x1, x2 = x[..., :h], x[..., h:]\n", "    x1, x2 = x[..., 0::2], x[..., 1::2]\n"),
+    ("query not rotated", "    qr = rope(q, pos, cos_sin)\n", "    qr = np.asarray(q, dtype=np.float64)\n"),
+    ("tree keys rotated by node index", "    kr = rope(k_tree, pos, cos_sin)\n", "    kr = rope(k_tree, np.arange(k_tree.shape[1])[None, :, None], cos_sin)\n"),
+    ("commit rotated at tree depth", "rope(k_tree[b, node, :, :], t, cos_sin)", "rope(k_tree[b, node, :, :], j, cos_sin)"),
 ]
 
 
@@ -101,8 +107,15 @@ def _pin_calls():
         calls.append(lambda s=s: T_ut.test_transitions_against_numpy_argmax_and_path(s))
     for s in range(6):
         calls.append(lambda s=s: T_ut.test_update_tree_is_the_update_of_its_pairs(s))
+    for D in [2, 16, 128]:
+        calls.append(lambda D=D: T_ro.test_rope_is_complex_multiplication(D))
+    calls.append(T_ro.test_rope_relative_positions_identity_and_norm)
+    for s in range(8):
+        calls.append(lambda s=s: T_ro.test_tree_attention_rope_brute_force(s))
+    calls.append(T_ro.test_append_kv_rope_commits_rotated_keys_at_cache_positions)
     calls += [T_sa.test_root_only_is_inverse_cdf_sampling,
-              T_sa.test_repeated_sibling_token_never_accepted]
+              T_sa.test_repeated_sibling_token_never_accepted,
+              T_sa.test_margins_on_a_hand_worked_case]
     for s in range(10):
         calls.append(lambda s=s: T_sa.test_low_temperature_is_greedy(s))
     calls.append(T_sa.test_lossless_first_and_second_token)
@@ -112,7 +125,7 @@ def _pin_calls():
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(name, old, new, monkeypatch):
     mod = _mutant_module(old, new)
-    for t in (T_bt, T_at, T_au, T_ap, T_ut, T_sa):
+    for t in (T_bt, T_at, T_au, T_ap, T_ut, T_ro, T_sa):
         monkeypatch.setattr(t, "O", mod)
     failed = 0
     for call in _pin_calls():

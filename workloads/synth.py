@@ -206,31 +206,33 @@ PRESETS = {
     "tiny_f32": dict(dtype="f32", B=1, Hq=4, Hkv=1, D=64, prefix=(128, 128),
                      kmax=16, stage_k_ret=[8, 4, 0], V=1000, S=4, n_draft=16,
                      max_tree_depth=5, conf="uniform", logit_std=1.0,
-                     table="identity", seed=1001),
+                     table="identity", seed=1001, rope_base=10000.0),
     # Llama-3-8B verify layer, batch 1.
     "llama3_8b_b1": dict(dtype="bf16", B=1, Hq=32, Hkv=8, D=128,
                          prefix=(2048, 2048), kmax=60, stage_k_ret=[32, 16, 0],
                          V=128256, S=8, n_draft=60, max_tree_depth=8,
                          conf="product", logit_std=2.0, table="identity",
-                         seed=1002),
+                         seed=1002, rope_base=500000.0),
     # Qwen3-8B batched verify: ragged prefixes, permuted pages.
     "qwen3_8b_b16": dict(dtype="bf16", B=16, Hq=32, Hkv=8, D=128,
                          prefix=(512, 4096), kmax=64, stage_k_ret=[32, 16, 0],
                          V=151936, S=8, n_draft=64, max_tree_depth=8,
                          conf="forced", logit_std=2.0, table="permuted",
-                         seed=1003),
+                         seed=1003, rope_base=1000000.0),
     # Llama-3.1-8B long context; M seeded from the prompt.
     "llama31_8b_64k": dict(dtype="bf16", B=1, Hq=32, Hkv=8, D=128,
                            prefix=(65536, 65536), kmax=64,
                            stage_k_ret=[32, 16, 0], V=128256, S=8, n_draft=64,
                            max_tree_depth=8, conf="product", logit_std=2.0,
-                           table="identity", seed=1004, seed_m_from_prompt=True),
+                           table="identity", seed=1004, seed_m_from_prompt=True,
+                           rope_base=500000.0),
     # Qwen3-235B-A22B attention, one GPU's head share; includes the M update.
     "qwen3_235b_share": dict(dtype="bf16", B=32, Hq=64, Hkv=4, D=128,
                              prefix=(8192, 8192), kmax=64,
                              stage_k_ret=[32, 16, 0], V=151936, S=8,
                              n_draft=64, max_tree_depth=8, conf="product",
-                             logit_std=2.0, table="identity", seed=1005),
+                             logit_std=2.0, table="identity", seed=1005,
+                             rope_base=1000000.0),
 }
 
 # The order of the five workloads as they are listed for this method.
@@ -391,3 +393,22 @@ def sampling_uniforms(seed: int, batch: int, n_max: int):
     ra = rng.random((batch, n_max), dtype=np.float32)
     rs = rng.random((batch, n_max), dtype=np.float32)
     return ra, rs
+
+
+def rope_table(positions: int, head_dim: int, base: float) -> np.ndarray:
+    """The caller-side rotary table [positions][head_dim] float32: row t holds
+    cos(t w_i) for i < head_dim / 2, then sin(t w_i), with frequencies
+    w_i = base^(-2 i / head_dim) (the published rotary embedding; angles in
+    float64, rounded to float32 once).  Llama-3.1's long-context frequency
+    rescaling would change only this table's contents."""
+    h = head_dim // 2
+    w = base ** (-2.0 * np.arange(h, dtype=np.float64) / head_dim)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * w[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def workload_rope_table(w) -> np.ndarray:
+    """The rotary table of a workload: every position up to the longest
+    prefix plus a whole tree."""
+    base = PRESETS.get(w.name, {}).get("rope_base", 10000.0)
+    return rope_table(int(w.max_prefix) + w.kmax + 2, w.D, base)
