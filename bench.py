@@ -230,7 +230,9 @@ def main():
                           w.plant_seed)
     base.logits.copy_(torch.from_numpy(logits.view(np.int16) if logits.dtype == np.uint16
                                        else logits).to(dev).view(base.logits.dtype))
-    # the random numbers of sampling acceptance (timed beside the step)
+    # the rotary table of the fused-RoPE variants and the random numbers of
+    # sampling acceptance (both timed beside the step)
+    base.set_rope(W.workload_rope_table(w))
     ra, rs = W.sampling_uniforms(w.plant_seed, w.B, base.n_max)
     base.rand_accept.copy_(torch.from_numpy(ra).to(dev))
     base.rand_sample.copy_(torch.from_numpy(rs).to(dev))
@@ -311,11 +313,14 @@ def main():
 
     # the next rows of the path, measured beside the step: committing the
     # accepted path's K/V to the cache (idempotent: same slots, same values),
-    # the all-node update of M, and sampling acceptance at temperature 1
-    # (last: it overwrites the accepted paths)
+    # the all-node update of M, the attention and the commit with the rotary
+    # embedding fused in, and sampling acceptance at temperature 1 (last: it
+    # overwrites the accepted paths)
     next_us = {}
     for name, call in (("append_kv", lambda s: s.append()),
                        ("update_tree", lambda s: s.update_tree()),
+                       ("attention_rope", lambda s: s.attention_rope()),
+                       ("append_kv_rope", lambda s: s.append_rope()),
                        ("accept_sample", lambda s: s.accept_sample(1.0))):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):

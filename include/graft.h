@@ -16,6 +16,9 @@
  *   graft_update_adjacency  online update of the successor table M
  *   graft_update_adjacency_tree  the same update from every verified node
  *   graft_append_kv         commit of the accepted path to the KV cache
+ *   graft_tree_attention_rope, graft_append_kv_rope
+ *                           the same two with the rotary position embedding
+ *                           fused into their key/query loads
  *
  * Conventions for every call
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -183,6 +186,43 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * graft_tree_attention_rope -- graft_tree_attention for unrotated queries
+ * and tree keys: the rotary position embedding at each node's tree position
+ * is fused into their loads (architecture paragraph: the tree-attention
+ * verify forward; positions prefix_len + depth as written by
+ * graft_build_tree).  The pages do not name the target's positional scheme;
+ * this is the published rotary embedding with the rotate-half pairing used
+ * by Llama 3 and Qwen3: for i < head_dim/2 the pair (x_i, x_{i+head_dim/2})
+ * becomes (x_i c - x_{i+head_dim/2} s, x_{i+head_dim/2} c + x_i s).
+ *
+ * Node i's query (every head) and key are rotated at position
+ * p = tree_pos[b][i]; the cached prefix keys are used as they are (rotated
+ * when they were written, e.g. by graft_append_kv_rope).
+ *   tree_pos       int32 [batch][n_max] (from graft_build_tree)
+ *   rope_cos_sin   float [rope_positions][head_dim], 16-byte aligned: row p
+ *                  holds cos(p w_i) for i < head_dim/2, then sin(p w_i)
+ *                  (any frequencies w_i, including rescaled ones)
+ * Positions outside [0, rope_positions) are a precondition violation; the
+ * kernels clamp them into the table.  The rotation is computed in fp32; on
+ * the matrix-core path the rotated bf16 inputs are rounded once to bf16
+ * before the dot products.  Everything else, workspace included, as
+ * graft_tree_attention.
+ */
+graft_status graft_tree_attention_rope(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                       int32_t hq, int32_t hkv, int32_t head_dim,
+                                       const void *q, const void *k_tree,
+                                       const void *v_tree, const void *k_cache,
+                                       const void *v_cache, int32_t block_size,
+                                       const int32_t *block_table,
+                                       int32_t max_blocks_per_seq,
+                                       const int32_t *prefix_len, int32_t max_prefix,
+                                       const uint32_t *tree_mask, const int32_t *n_nodes,
+                                       const int32_t *tree_pos, const float *rope_cos_sin,
+                                       int32_t rope_positions, float scale, void *out,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * graft_accept -- lossless greedy acceptance (architecture paragraph:
  * retrieval nodes are proposals like drafts and the output distribution is
  * preserved; abstract: lossless), read for greedy decoding.
@@ -347,6 +387,24 @@ graft_status graft_append_kv(graft_dtype dtype, int32_t batch, int32_t n_max, in
                              int32_t max_blocks_per_seq, const int32_t *prefix_len,
                              const int32_t *path_nodes, const int32_t *accept_len,
                              int32_t *new_prefix_len, hipStream_t stream);
+
+/*
+ * graft_append_kv_rope -- graft_append_kv for unrotated tree keys: the key
+ * committed to cache token t = prefix_len[b] + j is rotated at position t
+ * (the rotary embedding of graft_tree_attention_rope, computed in fp32 and
+ * rounded once to the cache dtype); values are copied.  rope_cos_sin and
+ * rope_positions as in graft_tree_attention_rope; head_dim even.
+ * Everything else as graft_append_kv.
+ */
+graft_status graft_append_kv_rope(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                  int32_t hkv, int32_t head_dim, const void *k_tree,
+                                  const void *v_tree, void *k_cache, void *v_cache,
+                                  int32_t num_blocks, int32_t block_size,
+                                  const int32_t *block_table, int32_t max_blocks_per_seq,
+                                  const int32_t *prefix_len, const int32_t *path_nodes,
+                                  const int32_t *accept_len, int32_t *new_prefix_len,
+                                  const float *rope_cos_sin, int32_t rope_positions,
+                                  hipStream_t stream);
 
 /* Message for the last non-OK status returned on this thread. */
 const char *graft_last_error(void);

@@ -27,7 +27,7 @@ def test_header_declares_the_calls():
     names = header_functions()
     for n in ["graft_build_tree", "graft_tree_attention", "graft_accept",
               "graft_accept_sample", "graft_update_adjacency", "graft_update_adjacency_tree",
-              "graft_append_kv"]:
+              "graft_append_kv", "graft_tree_attention_rope", "graft_append_kv_rope"]:
         assert n in names
 
 
@@ -182,3 +182,30 @@ def test_accept_sample_validation():
         assert lib.graft_accept_sample_workspace_size(dt, 2, 65, 151936) == want
     assert acc(v=2304 * 4096 + 1) == -2   # more chunks than one workgroup stages
     assert lib.graft_accept_sample_workspace_size(5, 2, 65, 151936) == 0
+
+
+def test_rope_variants_validation():
+    def att(**k):
+        return lib.graft_tree_attention_rope(
+            k.get("dt", 1), k.get("b", 1), k.get("n", 17), 32, 8, k.get("d", 128), *([FAKE] * 5),
+            16, FAKE, 8, FAKE, 128, FAKE, FAKE, k.get("tp", FAKE), k.get("rope", FAKE),
+            k.get("rp", 4096), ctypes.c_float(k.get("scale", 0.088)), FAKE, FAKE, 1 << 24, None)
+    assert att(rp=0) == -1
+    assert att(tp=None) == -1
+    assert att(rope=None) == -1
+    assert att(rope=ctypes.c_void_p(0x1004)) == -1        # table not 16-byte aligned
+    assert "aligned" in G.graft_last_error()
+    assert att(d=96) == -2                                # head_dim outside 64 / 128
+    assert att(scale=0.0) == -1
+    assert att(b=0) == 0
+
+    def app(**k):
+        return lib.graft_append_kv_rope(k.get("dt", 1), k.get("b", 2), 9, 2, k.get("d", 128),
+                                        FAKE, FAKE, FAKE, FAKE, 64, 16, FAKE, 8, FAKE, FAKE,
+                                        FAKE, ctypes.c_void_p(0x2000), k.get("rope", FAKE),
+                                        k.get("rp", 4096), None)
+    assert app(d=127) == -1
+    assert app(rp=0) == -1
+    assert app(rope=None) == -1
+    assert app(dt=9) == -1
+    assert app(b=0) == 0

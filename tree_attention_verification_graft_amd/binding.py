@@ -28,7 +28,8 @@ EXPORTED = [
     "graft_accept_sample_workspace_size", "graft_accept_sample",
     "graft_update_adjacency_workspace_size", "graft_update_adjacency",
     "graft_update_adjacency_tree_workspace_size", "graft_update_adjacency_tree",
-    "graft_append_kv", "graft_last_error", "graft_version",
+    "graft_append_kv", "graft_tree_attention_rope", "graft_append_kv_rope",
+    "graft_last_error", "graft_version",
 ]
 
 
@@ -95,6 +96,9 @@ def _load(path=LIB_PATH):
         "graft_update_adjacency_tree_workspace_size": [I, I],
         "graft_update_adjacency_tree": [P, P, I, I, I, I, P, P, P, P, SZ, P],
         "graft_append_kv": [I, I, I, I, I, P, P, P, P, I, I, P, I, P, P, P, P, P],
+        "graft_tree_attention_rope": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, P, P,
+                                      P, P, I, ctypes.c_float, P, P, SZ, P],
+        "graft_append_kv_rope": [I, I, I, I, I, P, P, P, P, I, I, P, I, P, P, P, P, P, I, P],
         "graft_last_error": [],
         "graft_version": [],
     }
@@ -217,6 +221,36 @@ def graft_tree_attention(q, k_tree, v_tree, k_cache, v_cache, block_table, prefi
     _check(st, "graft_tree_attention")
 
 
+def graft_tree_attention_rope(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
+                              max_prefix, tree_mask, n_nodes, tree_pos, rope_cos_sin, scale,
+                              out, workspace, stream=None):
+    B, n_max, hq, D = q.shape
+    hkv = k_tree.shape[2]
+    nblk, _, blk, _ = k_cache.shape
+    dt = _dtype_code(q)
+    for t, n in ((k_tree, "k_tree"), (v_tree, "v_tree")):
+        _expect(t, q.dtype, (B, n_max, hkv, D), n)
+    _expect(k_cache, q.dtype, (nblk, hkv, blk, D), "k_cache")
+    _expect(v_cache, q.dtype, (nblk, hkv, D, blk), "v_cache")
+    _expect(out, q.dtype, (B, n_max, hq, D), "out")
+    _expect(tree_mask, torch.int32, (B, n_max, mask_words(n_max)), "tree_mask")
+    _expect(tree_pos, torch.int32, (B, n_max), "tree_pos")
+    if rope_cos_sin.dtype != torch.float32 or rope_cos_sin.dim() != 2 or \
+            rope_cos_sin.shape[1] != D:
+        raise GraftError("rope_cos_sin: expected float32 [positions][head_dim]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise GraftError("block_table: expected int32 [batch][max_blocks]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.graft_tree_attention_rope(dt, B, n_max, hq, hkv, D, _ptr(q), _ptr(k_tree),
+                                        _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), blk,
+                                        _ptr(block_table), block_table.shape[1],
+                                        _ptr(prefix_len), int(max_prefix), _ptr(tree_mask),
+                                        _ptr(n_nodes), _ptr(tree_pos), _ptr(rope_cos_sin),
+                                        rope_cos_sin.shape[0], float(scale), _ptr(out),
+                                        _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "graft_tree_attention_rope")
+
+
 def graft_accept_workspace_size(batch, n_max, vocab):
     return int(_lib.graft_accept_workspace_size(batch, n_max, vocab))
 
@@ -328,6 +362,32 @@ def graft_append_kv(k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, p
                               _ptr(prefix_len), _ptr(path_nodes), _ptr(accept_len),
                               _ptr(new_prefix_len), _stream(stream))
     _check(st, "graft_append_kv")
+
+
+def graft_append_kv_rope(k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, path_nodes,
+                         accept_len, new_prefix_len, rope_cos_sin, stream=None):
+    B, n_max, hkv, D = k_tree.shape
+    nblk, _, blk, _ = k_cache.shape
+    dt = _dtype_code(k_tree)
+    i32 = torch.int32
+    _expect(v_tree, k_tree.dtype, (B, n_max, hkv, D), "v_tree")
+    _expect(k_cache, k_tree.dtype, (nblk, hkv, blk, D), "k_cache")
+    _expect(v_cache, k_tree.dtype, (nblk, hkv, D, blk), "v_cache")
+    _expect(path_nodes, i32, (B, n_max), "path_nodes")
+    for t, n in ((prefix_len, "prefix_len"), (accept_len, "accept_len"),
+                 (new_prefix_len, "new_prefix_len")):
+        _expect(t, i32, (B,), n)
+    if block_table.dtype != i32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise GraftError("block_table: expected int32 [batch][max_blocks]")
+    if rope_cos_sin.dtype != torch.float32 or rope_cos_sin.dim() != 2 or \
+            rope_cos_sin.shape[1] != D:
+        raise GraftError("rope_cos_sin: expected float32 [positions][head_dim]")
+    st = _lib.graft_append_kv_rope(dt, B, n_max, hkv, D, _ptr(k_tree), _ptr(v_tree),
+                                   _ptr(k_cache), _ptr(v_cache), nblk, blk, _ptr(block_table),
+                                   block_table.shape[1], _ptr(prefix_len), _ptr(path_nodes),
+                                   _ptr(accept_len), _ptr(new_prefix_len), _ptr(rope_cos_sin),
+                                   rope_cos_sin.shape[0], _stream(stream))
+    _check(st, "graft_append_kv_rope")
 
 
 def graft_last_error():

@@ -167,17 +167,17 @@ size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch, int
   return align_up(pl.part_o_bytes, 256) + align_up(pl.part_ml_bytes, 256);
 }
 
-graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_max,
-                                  int32_t hq, int32_t hkv, int32_t head_dim,
-                                  const void *q, const void *k_tree, const void *v_tree,
-                                  const void *k_cache, const void *v_cache,
-                                  int32_t block_size, const int32_t *block_table,
-                                  int32_t max_blocks_per_seq, const int32_t *prefix_len,
-                                  int32_t max_prefix, const uint32_t *tree_mask,
-                                  const int32_t *n_nodes, float scale, void *out,
-                                  void *workspace, size_t workspace_bytes,
-                                  hipStream_t stream) {
-  g_error[0] = 0;
+static graft_status attention_impl(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hq,
+                                   int32_t hkv, int32_t head_dim, const void *q,
+                                   const void *k_tree, const void *v_tree, const void *k_cache,
+                                   const void *v_cache, int32_t block_size,
+                                   const int32_t *block_table, int32_t max_blocks_per_seq,
+                                   const int32_t *prefix_len, int32_t max_prefix,
+                                   const uint32_t *tree_mask, const int32_t *n_nodes,
+                                   const int32_t *tree_pos, const float *rope,
+                                   int32_t rope_positions, float scale, void *out,
+                                   void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
   graft_status st = check_attn_shape(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
   if (st != GRAFT_OK) return st;
   REQUIRE(block_size == 16, GRAFT_ERR_UNSUPPORTED,
@@ -218,6 +218,9 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
   p.tree_mask = tree_mask;
   p.n_nodes = n_nodes;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.tree_pos = tree_pos;
+  p.rope = rope;
+  p.rope_positions = rope_positions;
   p.out = out;
   p.n_splits = pl.n_splits;
   p.tiles_per_split = pl.tiles_per_split;
@@ -238,6 +241,47 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
     if ((st = check_launch("graft_tree_attention (combine)")) != GRAFT_OK) return st;
   }
   return GRAFT_OK;
+}
+
+graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                  int32_t hq, int32_t hkv, int32_t head_dim,
+                                  const void *q, const void *k_tree, const void *v_tree,
+                                  const void *k_cache, const void *v_cache,
+                                  int32_t block_size, const int32_t *block_table,
+                                  int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                                  int32_t max_prefix, const uint32_t *tree_mask,
+                                  const int32_t *n_nodes, float scale, void *out,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  g_error[0] = 0;
+  return attention_impl(dtype, batch, n_max, hq, hkv, head_dim, q, k_tree, v_tree, k_cache,
+                        v_cache, block_size, block_table, max_blocks_per_seq, prefix_len,
+                        max_prefix, tree_mask, n_nodes, nullptr, nullptr, 0, scale, out,
+                        workspace, workspace_bytes, stream);
+}
+
+graft_status graft_tree_attention_rope(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                       int32_t hq, int32_t hkv, int32_t head_dim,
+                                       const void *q, const void *k_tree, const void *v_tree,
+                                       const void *k_cache, const void *v_cache,
+                                       int32_t block_size, const int32_t *block_table,
+                                       int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                                       int32_t max_prefix, const uint32_t *tree_mask,
+                                       const int32_t *n_nodes, const int32_t *tree_pos,
+                                       const float *rope_cos_sin, int32_t rope_positions,
+                                       float scale, void *out, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(rope_positions >= 1, GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention_rope: rope_positions < 1");
+  REQUIRE(batch == 0 || (tree_pos && rope_cos_sin), GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention_rope: null device pointer");
+  REQUIRE(((uintptr_t)rope_cos_sin & 15) == 0, GRAFT_ERR_INVALID_ARG,
+          "graft_tree_attention_rope: the table must be 16-byte aligned");
+  return attention_impl(dtype, batch, n_max, hq, hkv, head_dim, q, k_tree, v_tree, k_cache,
+                        v_cache, block_size, block_table, max_blocks_per_seq, prefix_len,
+                        max_prefix, tree_mask, n_nodes, tree_pos, rope_cos_sin, rope_positions,
+                        scale, out, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------------------------- accept
@@ -464,14 +508,14 @@ graft_status graft_update_adjacency_tree(int32_t *m_ids, float *m_scores, int32_
 }
 
 // ---------------------------------------------------------------- KV append
-graft_status graft_append_kv(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hkv,
-                             int32_t head_dim, const void *k_tree, const void *v_tree,
-                             void *k_cache, void *v_cache, int32_t num_blocks,
-                             int32_t block_size, const int32_t *block_table,
-                             int32_t max_blocks_per_seq, const int32_t *prefix_len,
-                             const int32_t *path_nodes, const int32_t *accept_len,
-                             int32_t *new_prefix_len, hipStream_t stream) {
-  g_error[0] = 0;
+static graft_status append_impl(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hkv,
+                                int32_t head_dim, const void *k_tree, const void *v_tree,
+                                void *k_cache, void *v_cache, int32_t num_blocks,
+                                int32_t block_size, const int32_t *block_table,
+                                int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                                const int32_t *path_nodes, const int32_t *accept_len,
+                                int32_t *new_prefix_len, const float *rope,
+                                int32_t rope_positions, hipStream_t stream) {
   REQUIRE(dtype == GRAFT_F32 || dtype == GRAFT_BF16, GRAFT_ERR_INVALID_ARG,
           "graft_append_kv: unknown dtype %d", (int)dtype);
   REQUIRE(batch >= 0 && n_max >= 1 && n_max <= GRAFT_MAX_NODES && hkv >= 1 && head_dim >= 1,
@@ -503,8 +547,42 @@ graft_status graft_append_kv(graft_dtype dtype, int32_t batch, int32_t n_max, in
   p.path_nodes = path_nodes;
   p.accept_len = accept_len;
   p.new_prefix_len = new_prefix_len;
+  p.rope = rope;
+  p.rope_positions = rope_positions;
   launch_append_kv(dtype, p, stream);
   return check_launch("graft_append_kv");
+}
+
+graft_status graft_append_kv(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hkv,
+                             int32_t head_dim, const void *k_tree, const void *v_tree,
+                             void *k_cache, void *v_cache, int32_t num_blocks,
+                             int32_t block_size, const int32_t *block_table,
+                             int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                             const int32_t *path_nodes, const int32_t *accept_len,
+                             int32_t *new_prefix_len, hipStream_t stream) {
+  g_error[0] = 0;
+  return append_impl(dtype, batch, n_max, hkv, head_dim, k_tree, v_tree, k_cache, v_cache,
+                     num_blocks, block_size, block_table, max_blocks_per_seq, prefix_len,
+                     path_nodes, accept_len, new_prefix_len, nullptr, 0, stream);
+}
+
+graft_status graft_append_kv_rope(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hkv,
+                                  int32_t head_dim, const void *k_tree, const void *v_tree,
+                                  void *k_cache, void *v_cache, int32_t num_blocks,
+                                  int32_t block_size, const int32_t *block_table,
+                                  int32_t max_blocks_per_seq, const int32_t *prefix_len,
+                                  const int32_t *path_nodes, const int32_t *accept_len,
+                                  int32_t *new_prefix_len, const float *rope_cos_sin,
+                                  int32_t rope_positions, hipStream_t stream) {
+  g_error[0] = 0;
+  REQUIRE(head_dim % 2 == 0, GRAFT_ERR_INVALID_ARG, "graft_append_kv_rope: odd head_dim");
+  REQUIRE(rope_positions >= 1, GRAFT_ERR_INVALID_ARG, "graft_append_kv_rope: rope_positions < 1");
+  REQUIRE(batch == 0 || rope_cos_sin, GRAFT_ERR_INVALID_ARG,
+          "graft_append_kv_rope: null device pointer");
+  return append_impl(dtype, batch, n_max, hkv, head_dim, k_tree, v_tree, k_cache, v_cache,
+                     num_blocks, block_size, block_table, max_blocks_per_seq, prefix_len,
+                     path_nodes, accept_len, new_prefix_len, rope_cos_sin, rope_positions,
+                     stream);
 }
 
 }  // extern "C"

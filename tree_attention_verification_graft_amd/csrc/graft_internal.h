@@ -54,6 +54,11 @@ struct AttnParams {
   const uint32_t *tree_mask;
   const int32_t *n_nodes;
   float scale_log2;  // scale * log2(e)
+  // rotary embedding of queries and tree keys on load (rope == nullptr: the
+  // inputs arrive rotated): table [rope_positions][head_dim] of cos | sin
+  const int32_t *tree_pos;
+  const float *rope;
+  int32_t rope_positions;
   void *out;
   // split-K plan
   int32_t n_splits;        // prefix splits per (sequence, kv head, row group)
@@ -176,6 +181,8 @@ struct AppendParams {
   const int32_t *path_nodes;
   const int32_t *accept_len;
   int32_t *new_prefix_len;
+  const float *rope;       // nullptr: keys arrive rotated
+  int32_t rope_positions;
 };
 void launch_append_kv(graft_dtype dtype, const AppendParams &p, hipStream_t stream);
 

@@ -7,6 +7,10 @@
 // copies those rows: K into token-major pages (each row contiguous), V into
 // dim-major pages (one element per dim row of the page).
 //
+// With a rotary table the tree keys arrive unrotated, and the key committed
+// to cache token t is rotated at position t (rotate-half pairing of dim i
+// with dim i + D/2, in fp32, rounded once to the cache type).
+//
 // Method: "Draft Less, Retrieve More" (aitrends.kr summary), architecture
 // paragraph (one target forward verifies the hybrid tree; decoding continues
 // from the accepted tokens).
@@ -17,7 +21,16 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T>
+__device__ inline float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ inline float to_f32(uint32_t x) { return __uint_as_float(x); }
+__device__ inline void from_f32(float f, uint16_t &out) {
+  // round to nearest even (finite inputs)
+  const uint32_t u = __float_as_uint(f);
+  out = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ inline void from_f32(float f, uint32_t &out) { out = __float_as_uint(f); }
+
+template <typename T, bool ROPE>
 __global__ __launch_bounds__(kThreads) void append_kv_kernel(AppendParams p) {
   const int b = blockIdx.x / p.hkv;
   const int h = blockIdx.x % p.hkv;
@@ -41,7 +54,20 @@ __global__ __launch_bounds__(kThreads) void append_kv_kernel(AppendParams p) {
     const int slot = (int)(t % p.block_size);
     const size_t src = (((size_t)b * p.n_max + node) * p.hkv + h) * D + d;
     const size_t ph = (size_t)page * p.hkv + h;
-    k_cache[(ph * p.block_size + slot) * D + d] = k_tree[src];
+    if (ROPE) {
+      // pair (i, i + D/2) at cache position t
+      const int half = D / 2;
+      const int i = d < half ? d : d - half;
+      const float *row = p.rope + (size_t)min((long)p.rope_positions - 1, t) * D;
+      const float c = row[i], sn = row[half + i];
+      const float x = to_f32(k_tree[src]);
+      const float y = to_f32(k_tree[src - d + (d < half ? d + half : d - half)]);
+      T out;
+      from_f32(d < half ? x * c - y * sn : x * c + y * sn, out);
+      k_cache[(ph * p.block_size + slot) * D + d] = out;
+    } else {
+      k_cache[(ph * p.block_size + slot) * D + d] = k_tree[src];
+    }
     v_cache[(ph * D + d) * p.block_size + slot] = v_tree[src];
   }
 }
@@ -50,10 +76,13 @@ __global__ __launch_bounds__(kThreads) void append_kv_kernel(AppendParams p) {
 
 void launch_append_kv(graft_dtype dtype, const AppendParams &p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.batch * p.hkv));
-  if (dtype == GRAFT_BF16)
-    hipLaunchKernelGGL(append_kv_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(append_kv_kernel<uint32_t>, grid, dim3(kThreads), 0, stream, p);
+  if (dtype == GRAFT_BF16) {
+    if (p.rope) hipLaunchKernelGGL((append_kv_kernel<uint16_t, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((append_kv_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (p.rope) hipLaunchKernelGGL((append_kv_kernel<uint32_t, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((append_kv_kernel<uint32_t, false>), grid, dim3(kThreads), 0, stream, p);
+  }
 }
 
 }  // namespace graft

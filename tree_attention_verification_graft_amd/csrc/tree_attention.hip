@@ -21,6 +21,12 @@
 //
 // Wavefront path (fp32, or fewer than 16 query rows): one wave per query
 // row, keys spread over lanes for q.k, head dims over lanes for P V.
+//
+// Both paths optionally rotate the queries and the tree keys by their tree
+// positions on load (rotary embedding, rotate-half pairing of dim i with
+// dim i + D/2, cosines and sines from a caller table), so that unrotated
+// projections need no separate pass; the cached prefix keys were rotated
+// when they were written.
 #include <hip/hip_bf16.h>
 
 #include <algorithm>
@@ -43,6 +49,30 @@ constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kMaxNB = 3;          // 16-row blocks per wave
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cosines and sines of dims i0 .. i0 + 7 at table row `pos` (a row holds
+// D/2 cosines, then D/2 sines).
+struct Rot8 {
+  float c[8], s[8];
+};
+__device__ inline Rot8 load_rot8(const float *rope, int D, int pos, int i0) {
+  const float *row = rope + (size_t)pos * D;
+  const float4 c0 = *reinterpret_cast<const float4 *>(row + i0);
+  const float4 c1 = *reinterpret_cast<const float4 *>(row + i0 + 4);
+  const float4 s0 = *reinterpret_cast<const float4 *>(row + D / 2 + i0);
+  const float4 s1 = *reinterpret_cast<const float4 *>(row + D / 2 + i0 + 4);
+  Rot8 r;
+  r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
+  r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
+  r.s[0] = s0.x; r.s[1] = s0.y; r.s[2] = s0.z; r.s[3] = s0.w;
+  r.s[4] = s1.x; r.s[5] = s1.y; r.s[6] = s1.z; r.s[7] = s1.w;
+  return r;
+}
+// Table row of a tree position (clamped into the table: positions outside
+// it are a caller error, and the clamp only keeps reads in bounds).
+__device__ inline int rope_row(const AttnParams &p, int b, int node) {
+  return min(max(p.tree_pos[(size_t)b * p.n_max + node], 0), p.rope_positions - 1);
+}
 
 // Maximum of two finite-or-(-inf) floats as one v_med3_f32 (median of a, b
 // and +inf); unlike fmaxf it needs no NaN canonicalisation of its inputs.
@@ -186,7 +216,7 @@ struct MfmaCtx {
 // One wave's share, specialised on the number NA of 16-row query blocks it
 // owns (wave-uniform), so that no matrix instruction sits behind a per-block
 // branch.  Every wave runs the same loads and barriers whatever NA is.
-template <int NA>
+template <int NA, bool ROPE>
 __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
                                                uint8_t *smem) {
   constexpr int NQ = NA > 0 ? NA : 1;
@@ -222,6 +252,24 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     for (int kk = 0; kk < 4; ++kk) {
       uint4 v = rv ? *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g4) : zero4();
       qf[k][kk] = *reinterpret_cast<bf16x8 *>(&v);
+    }
+    if (ROPE) {
+      // the lane holds dims 32 kk + 8 g4 + j; kk and kk + 2 are the pairs
+      // (i, i + 64), rotated in fp32 and rounded once to bf16
+      const int pos = rope_row(p, c.b, node);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const Rot8 r = load_rot8(p.rope, kD, pos, 32 * kk + 8 * g4);
+        bf16x8 a = qf[k][kk], e = qf[k][kk + 2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x1 = (float)a[j], x2 = (float)e[j];
+          a[j] = (__bf16)(x1 * r.c[j] - x2 * r.s[j]);
+          e[j] = (__bf16)(x2 * r.c[j] + x1 * r.s[j]);
+        }
+        qf[k][kk] = a;
+        qf[k][kk + 2] = e;
+      }
     }
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[k][d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -480,6 +528,25 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       if (j < c.n_nodes)
         kv = *reinterpret_cast<const uint4 *>(
             k_tree + (((size_t)c.b * p.n_max + j) * p.hkv + c.h) * kD + dc * 8);
+      if (ROPE) {
+        // dims 8 dc .. + 7 pair with dims 8 (dc ^ 8) .. + 7, held by lane ^ 8
+        // (same key): x' = x c - y s in the first half, x c + y s in the second
+        uint4 pv;
+        pv.x = __shfl_xor((int)kv.x, 8);
+        pv.y = __shfl_xor((int)kv.y, 8);
+        pv.z = __shfl_xor((int)kv.z, 8);
+        pv.w = __shfl_xor((int)kv.w, 8);
+        const Rot8 r = load_rot8(p.rope, kD, j < c.n_nodes ? rope_row(p, c.b, j) : 0,
+                                 8 * (dc & 7));
+        const float sg = dc < 8 ? -1.f : 1.f;
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(&kv);
+        const bf16x8 y = *reinterpret_cast<const bf16x8 *>(&pv);
+        bf16x8 o8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o8[e] = (__bf16)((float)x[e] * r.c[e] + sg * ((float)y[e] * r.s[e]));
+        kv = *reinterpret_cast<const uint4 *>(&o8);
+      }
       const int R = k_row_of_key(kl);
       *reinterpret_cast<uint4 *>(sK + R * 256 + ((dc ^ (R & 15)) << 4)) = kv;
     }
@@ -559,7 +626,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   }
 }
 
-template <int NB>
+template <int NB, bool ROPE>
 __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
@@ -619,10 +686,10 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
     const int rl = 16 * (c.wave + kMfmaWaves * k);
     if (rl < p.rows_per_group && c.row0 + rl < c.rows_b) na = k + 1;
   }
-  if (NB >= 3 && na == 3) mfma_wave_body<3>(p, c, smem);
-  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1)>(p, c, smem);
-  else if (na == 1) mfma_wave_body<1>(p, c, smem);
-  else mfma_wave_body<0>(p, c, smem);
+  if (NB >= 3 && na == 3) mfma_wave_body<3, ROPE>(p, c, smem);
+  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1), ROPE>(p, c, smem);
+  else if (na == 1) mfma_wave_body<1, ROPE>(p, c, smem);
+  else mfma_wave_body<0, ROPE>(p, c, smem);
 }
 
 // ------------------------------------------------------------------------
@@ -630,7 +697,7 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
 // Each lane scores one key of a 64-key chunk (a full dot product over the
 // head dim), then the lanes own head dims for the P V accumulation.  Dim-major
 // V pages make the per-dim key runs contiguous.
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnParams p) {
   constexpr int DPL = D / 64;  // head dims per lane
   __shared__ float s_q[4][D];
@@ -667,6 +734,17 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnParams p) {
 
   const T *qrow = q + (((size_t)b * p.n_max + node) * p.hq + hq) * D;
   for (int d = lane; d < D; d += 64) s_q[wave][d] = row_ok ? (float)qrow[d] : 0.f;
+  if (ROPE) {
+    // each lane rotates its own pairs (i, i + D/2) in place, kept in fp32
+    __builtin_amdgcn_wave_barrier();
+    const float *rrow = p.rope + (size_t)rope_row(p, b, node) * D;
+    for (int i = lane; i < D / 2; i += 64) {
+      const float c = rrow[i], sn = rrow[D / 2 + i];
+      const float x1 = s_q[wave][i], x2 = s_q[wave][i + D / 2];
+      s_q[wave][i] = x1 * c - x2 * sn;
+      s_q[wave][i + D / 2] = x2 * c + x1 * sn;
+    }
+  }
   uint32_t mw[GRAFT_MAX_NODES / 32] = {0u, 0u, 0u, 0u};
   if (row_ok) load_mask4(mw, p.tree_mask + ((size_t)b * p.n_max + node) * p.words, p.words);
   __syncthreads();
@@ -692,7 +770,17 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnParams p) {
     float sc = -INFINITY;
     if (vis && row_ok) {
       float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot += s_q[wave][d] * (float)krow[d];
+      if (ROPE && tree) {
+        // the tree key rotated at its own position, pair by pair
+        const float *rrow = p.rope + (size_t)rope_row(p, b, key) * D;
+        for (int i = 0; i < D / 2; ++i) {
+          const float k1 = (float)krow[i], k2 = (float)krow[i + D / 2];
+          const float c = rrow[i], sn = rrow[D / 2 + i];
+          dot += s_q[wave][i] * (k1 * c - k2 * sn) + s_q[wave][i + D / 2] * (k2 * c + k1 * sn);
+        }
+      } else {
+        for (int d = 0; d < D; ++d) dot += s_q[wave][d] * (float)krow[d];
+      }
       sc = dot * p.scale_log2;
     }
     float mx = sc;
@@ -951,24 +1039,39 @@ void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream) {
   dim3 grid((unsigned)(8 * p.n_row_groups * ((clusters + 7) / 8)));
   const int nb = (p.rows_per_group / 16 + kMfmaWaves - 1) / kMfmaWaves;
   switch (nb) {
-    case 1: hipLaunchKernelGGL(attn_mfma_kernel<1>, grid, dim3(kMfmaThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(attn_mfma_kernel<2>, grid, dim3(kMfmaThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL(attn_mfma_kernel<3>, grid, dim3(kMfmaThreads), 0, stream, p); break;
+    case 1:
+      if (p.rope) hipLaunchKernelGGL((attn_mfma_kernel<1, true>), grid, dim3(kMfmaThreads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_mfma_kernel<1, false>), grid, dim3(kMfmaThreads), 0, stream, p);
+      break;
+    case 2:
+      if (p.rope) hipLaunchKernelGGL((attn_mfma_kernel<2, true>), grid, dim3(kMfmaThreads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_mfma_kernel<2, false>), grid, dim3(kMfmaThreads), 0, stream, p);
+      break;
+    default:
+      if (p.rope) hipLaunchKernelGGL((attn_mfma_kernel<3, true>), grid, dim3(kMfmaThreads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_mfma_kernel<3, false>), grid, dim3(kMfmaThreads), 0, stream, p);
+      break;
   }
 }
+
+namespace {
+template <typename T, int D>
+void launch_wave(const AttnParams &p, dim3 grid, hipStream_t stream) {
+  if (p.rope)
+    hipLaunchKernelGGL((attn_wave_kernel<T, D, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_wave_kernel<T, D, false>), grid, dim3(kThreads), 0, stream, p);
+}
+}  // namespace
 
 void launch_attention_wave(graft_dtype dtype, const AttnParams &p, hipStream_t stream) {
   dim3 grid(p.n_splits, p.hkv * (p.rows_per_group / 4), p.batch);
   if (dtype == GRAFT_F32) {
-    if (p.head_dim == 64)
-      hipLaunchKernelGGL((attn_wave_kernel<float, 64>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_wave_kernel<float, 128>), grid, dim3(kThreads), 0, stream, p);
+    if (p.head_dim == 64) launch_wave<float, 64>(p, grid, stream);
+    else launch_wave<float, 128>(p, grid, stream);
   } else {
-    if (p.head_dim == 64)
-      hipLaunchKernelGGL((attn_wave_kernel<__hip_bfloat16, 64>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_wave_kernel<__hip_bfloat16, 128>), grid, dim3(kThreads), 0, stream, p);
+    if (p.head_dim == 64) launch_wave<__hip_bfloat16, 64>(p, grid, stream);
+    else launch_wave<__hip_bfloat16, 128>(p, grid, stream);
   }
 }
 

@@ -125,6 +125,22 @@ class DeviceStep:
         G.graft_update_adjacency_tree(self.m_ids, self.m_scores, self.tree_token, self.argmax,
                                       self.n_nodes, self.update_tree_ws)
 
+    def set_rope(self, table):
+        """The rotary table [positions][head_dim] float32 for the fused
+        variants (q, k_tree then hold unrotated projections)."""
+        self.rope = torch.from_numpy(np.ascontiguousarray(table, np.float32)).to(self.dev)
+
+    def attention_rope(self):
+        G.graft_tree_attention_rope(self.q, self.k_tree, self.v_tree, self.k_cache, self.v_cache,
+                                    self.block_table, self.prefix_len, self.w.max_prefix,
+                                    self.tree_mask, self.n_nodes, self.tree_pos, self.rope,
+                                    self.w.scale, self.out, self.attn_ws)
+
+    def append_rope(self):
+        G.graft_append_kv_rope(self.k_tree, self.v_tree, self.k_cache, self.v_cache,
+                               self.block_table, self.prefix_len, self.path_nodes,
+                               self.accept_len, self.new_prefix_len, self.rope)
+
     def append(self):
         G.graft_append_kv(self.k_tree, self.v_tree, self.k_cache, self.v_cache,
                           self.block_table, self.prefix_len, self.path_nodes, self.accept_len,
