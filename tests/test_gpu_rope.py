@@ -177,7 +177,7 @@ def test_unit_table_equals_the_unrotated_call():
     """With cos = 1 and sin = 0 everywhere the fused call is the plain one, bit
     for bit (the rotation in fp32 of a bf16 value times 1 is exact)."""
     import torch
-    w = W.make("qwen3_8b_b16", **SMALL["qwen3_8b_b16"])
+    w = W.make("llama3_8b_b1", **SMALL["llama3_8b_b1"])
     ds, t, _ = _step(w, plant=False)
     table = np.zeros((int(w.max_prefix) + w.kmax + 2, w.D), np.float32)
     table[:, :w.D // 2] = 1.0

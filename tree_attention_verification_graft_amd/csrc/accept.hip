@@ -34,6 +34,13 @@ constexpr int kLargeGrid = 8192;    // workgroups above which chunks grow
 template <bool BF16, int L>
 constexpr int chunk_len() { return L * kThreads * (BF16 ? 8 : 4); }
 constexpr int kPathThreads = 256; // >= GRAFT_MAX_NODES
+constexpr int kKeyBatch = 16;     // chunk keys per thread loaded at once
+
+// Workgroup barrier that waits for LDS operations only: global loads issued
+// before it stay in flight (a full __syncthreads also drains them).
+__device__ __forceinline__ void lds_only_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
 
 __device__ inline uint32_t ord_bf16(uint32_t u) {
   if (u == 0x8000u) u = 0;  // -0 == +0
@@ -152,14 +159,34 @@ __global__ __launch_bounds__(kPathThreads) void accept_path_kernel(AcceptParams 
 #pragma unroll
     for (int w = 0; w < 4; ++w) mw[w] = w < p.words ? mrow[w] : 0u;
   }
-  if (i < GRAFT_MAX_NODES) s_key[i] = 0ull;
-  __syncthreads();
-  // chunk keys of all rows, folded per row (rows past the tree are folded
-  // too and ignored below)
+  // chunk keys of all rows (rows past the tree are folded too and ignored
+  // below): the first kKeyBatch per thread are loaded with the tree arrays,
+  // before a barrier that waits only for LDS, so every load of the kernel
+  // is in flight at once
   const int total = p.n_max * p.chunks;
   const unsigned long long *part = p.partial + (size_t)b * total;
-#pragma unroll 4
-  for (int k = i; k < total; k += kPathThreads) atomicMax(&s_key[k / p.chunks], part[k]);
+  unsigned long long kb[kKeyBatch];
+#pragma unroll
+  for (int j = 0; j < kKeyBatch; ++j) {
+    const int k = i + j * kPathThreads;
+    kb[j] = k < total ? part[k] : 0ull;
+  }
+  if (i < GRAFT_MAX_NODES) s_key[i] = 0ull;
+  lds_only_barrier();
+  for (int k0 = 0; k0 < total; k0 += kKeyBatch * kPathThreads) {
+    if (k0 > 0) {
+#pragma unroll
+      for (int j = 0; j < kKeyBatch; ++j) {
+        const int k = k0 + i + j * kPathThreads;
+        kb[j] = k < total ? part[k] : 0ull;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kKeyBatch; ++j) {
+      const int k = k0 + i + j * kPathThreads;
+      if (k < total) atomicMax(&s_key[k / p.chunks], kb[j]);
+    }
+  }
   __syncthreads();
 
   const bool live = in_row && i < n_nodes;

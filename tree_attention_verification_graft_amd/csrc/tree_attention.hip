@@ -211,6 +211,10 @@ struct MfmaCtx {
   // clamped to the table row; entries past the prefix are replaced later).
   int pre_page[3];
   int first_page;
+  // rotary embedding: tree positions of the wave's query rows and of node
+  // `tid` (loaded with the first round of scalar loads)
+  int qpos[kMaxNB];
+  int tpos;
 };
 
 // One wave's share, specialised on the number NA of 16-row query blocks it
@@ -218,7 +222,7 @@ struct MfmaCtx {
 // branch.  Every wave runs the same loads and barriers whatever NA is.
 template <int NA, bool ROPE>
 __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
-                                               uint8_t *smem) {
+                                               uint8_t *smem, int32_t *s_tpos) {
   constexpr int NQ = NA > 0 ? NA : 1;
   // V operands read ahead of the softmax (all eight where registers allow)
   constexpr int kVPre = NA >= 2 ? 4 : 8;
@@ -253,29 +257,26 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       uint4 v = rv ? *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g4) : zero4();
       qf[k][kk] = *reinterpret_cast<bf16x8 *>(&v);
     }
-    if (ROPE) {
-      // the lane holds dims 32 kk + 8 g4 + j; kk and kk + 2 are the pairs
-      // (i, i + 64), rotated in fp32 and rounded once to bf16
-      const int pos = rope_row(p, c.b, node);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const Rot8 r = load_rot8(p.rope, kD, pos, 32 * kk + 8 * g4);
-        bf16x8 a = qf[k][kk], e = qf[k][kk + 2];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x1 = (float)a[j], x2 = (float)e[j];
-          a[j] = (__bf16)(x1 * r.c[j] - x2 * r.s[j]);
-          e[j] = (__bf16)(x2 * r.c[j] + x1 * r.s[j]);
-        }
-        qf[k][kk] = a;
-        qf[k][kk + 2] = e;
-      }
-    }
+
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[k][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[k] = kNegBig;
     thr_raw[k] = kNegBig;  // the first scores always set the offset
     l_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // rotary embedding of the queries: the table rows are loaded with the
+  // queries and the rotation waits until the prologue's own wait below;
+  // with three blocks per wave the registers do not allow holding them, so
+  // they are loaded after that wait instead
+  constexpr bool kEarlyRot = NA <= 2;
+  Rot8 rq[ROPE && kEarlyRot ? NQ : 1][2];
+  if (ROPE && kEarlyRot) {
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
+      const int pos = min(max(c.qpos[k], 0), p.rope_positions - 1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) rq[k][kk] = load_rot8(p.rope, kD, pos, 32 * kk + 8 * g4);
+    }
   }
 
   // ---- asynchronous loads of the prefix tiles.  Every wave loads one page
@@ -473,6 +474,32 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   if (c.n_pref > 1) issue_prefix(1, fix_page(c.pre_page[1], 1));
   if (c.n_pref > 2) page_next = fix_page(c.pre_page[2], 2);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries and stages 0, 1
+  if (ROPE) {
+    // the lane holds dims 32 kk + 8 g4 + j; kk and kk + 2 are the pairs
+    // (i, i + 64), rotated in fp32 and rounded once to bf16
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const Rot8 r = kEarlyRot ? rq[kEarlyRot ? k : 0][kk]
+                                 : load_rot8(p.rope, kD,
+                                             min(max(c.qpos[k], 0), p.rope_positions - 1),
+                                             32 * kk + 8 * g4);
+        bf16x8 a = qf[k][kk], e = qf[k][kk + 2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x1 = (float)a[j], x2 = (float)e[j];
+          a[j] = (__bf16)(x1 * r.c[j] - x2 * r.s[j]);
+          e[j] = (__bf16)(x2 * r.c[j] + x1 * r.s[j]);
+        }
+        qf[k][kk] = a;
+        qf[k][kk + 2] = e;
+      }
+    }
+    // tree positions for the tree tiles (published by the loop's first
+    // barrier)
+    if (tid < p.n_max) s_tpos[tid] = c.tpos;
+  }
   if (c.n_pref > 2) issue_prefix(2, page_next);
   if (c.n_pref > 3) page_next = tile_page(3);
   for (int it = 0; it < c.n_pref; ++it) {
@@ -524,6 +551,12 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       const int ch = tid + kMfmaThreads * r;
       const int kl = ch >> 4, dc = ch & 15;
       const int j = key0 + kl;
+      Rot8 rk;
+      if (ROPE) {
+        // the table row first, so that it loads alongside the key chunk
+        const int pos = j < c.n_nodes ? min(max(s_tpos[j], 0), p.rope_positions - 1) : 0;
+        rk = load_rot8(p.rope, kD, pos, 8 * (dc & 7));
+      }
       uint4 kv = zero4();
       if (j < c.n_nodes)
         kv = *reinterpret_cast<const uint4 *>(
@@ -536,15 +569,13 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
         pv.y = __shfl_xor((int)kv.y, 8);
         pv.z = __shfl_xor((int)kv.z, 8);
         pv.w = __shfl_xor((int)kv.w, 8);
-        const Rot8 r = load_rot8(p.rope, kD, j < c.n_nodes ? rope_row(p, c.b, j) : 0,
-                                 8 * (dc & 7));
         const float sg = dc < 8 ? -1.f : 1.f;
         const bf16x8 x = *reinterpret_cast<const bf16x8 *>(&kv);
         const bf16x8 y = *reinterpret_cast<const bf16x8 *>(&pv);
         bf16x8 o8;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          o8[e] = (__bf16)((float)x[e] * r.c[e] + sg * ((float)y[e] * r.s[e]));
+          o8[e] = (__bf16)((float)x[e] * rk.c[e] + sg * ((float)y[e] * rk.s[e]));
         kv = *reinterpret_cast<const uint4 *>(&o8);
       }
       const int R = k_row_of_key(kl);
@@ -629,6 +660,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
 template <int NB, bool ROPE>
 __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  __shared__ int32_t s_tpos[ROPE ? GRAFT_MAX_NODES : 1];  // tree positions (rotary path)
 
   // XCD-aware decode: workgroups are dispatched to the 8 XCDs round-robin,
   // so id = xcd + 8 * slot.  The row groups of one KV stream (sequence,
@@ -648,6 +680,16 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  if (ROPE) {
+    // before the node count is known: indices clamped to the row
+    const int32_t *tp = p.tree_pos + (size_t)c.b * p.n_max;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int r = c.rg * p.rows_per_group + 16 * (c.wave + kMfmaWaves * k) + (c.lane & 15);
+      c.qpos[k] = tp[min(r / p.group, p.n_max - 1)];
+    }
+    c.tpos = c.tid < p.n_max ? tp[c.tid] : 0;
+  }
   {
     typedef const __attribute__((address_space(4))) int32_t const_i32;
     const_i32 *trow = (const_i32 *)(p.block_table + (size_t)c.b * p.max_blocks);
@@ -686,10 +728,10 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
     const int rl = 16 * (c.wave + kMfmaWaves * k);
     if (rl < p.rows_per_group && c.row0 + rl < c.rows_b) na = k + 1;
   }
-  if (NB >= 3 && na == 3) mfma_wave_body<3, ROPE>(p, c, smem);
-  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1), ROPE>(p, c, smem);
-  else if (na == 1) mfma_wave_body<1, ROPE>(p, c, smem);
-  else mfma_wave_body<0, ROPE>(p, c, smem);
+  if (NB >= 3 && na == 3) mfma_wave_body<3, ROPE>(p, c, smem, s_tpos);
+  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1), ROPE>(p, c, smem, s_tpos);
+  else if (na == 1) mfma_wave_body<1, ROPE>(p, c, smem, s_tpos);
+  else mfma_wave_body<0, ROPE>(p, c, smem, s_tpos);
 }
 
 // ------------------------------------------------------------------------
