@@ -38,6 +38,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified tree tokens/s + tree-attn KV-read HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0         # dense bf16 matrix-core peak
+STREAM_BYTES = 2 << 30            # read by the streaming-ceiling reduction
 DEFAULT_CONFIG = "llama3_8b_b1"   # the Llama-3-8B verify layer, batch 1
 ROTATE_BYTES = 600 << 20          # rotate input sets beyond the 256 MB MALL
 ATTN_SRC = os.path.join(ROOT, "tree_attention_verification_graft_amd", "csrc",
@@ -60,6 +62,19 @@ def attention_bytes(w, n_nodes):
     kv_tree = int(np.sum(n_nodes)) * w.Hkv * w.D * 2 * e
     q_out = int(np.sum(n_nodes)) * w.Hq * w.D * 2 * e
     return kv_prefix + kv_tree, q_out
+
+
+def attention_flops(w, n_nodes, masks):
+    """Algorithmic flops of one attention launch: q.k and p.v (2 D each) for
+    every (query row, visible key) pair; prefix keys are visible to every
+    row, tree keys to the row's ancestors-or-self (mask popcount)."""
+    G = w.Hq // w.Hkv
+    total = 0
+    for b in range(w.B):
+        n = int(n_nodes[b])
+        vis_tree = sum(bin(int(x)).count("1") for x in masks[b, :n].reshape(-1))
+        total += (int(w.prefix_len[b]) * n + vis_tree) * G * w.Hkv * 4 * w.D
+    return total
 
 
 def kernel_source_sha():
@@ -345,6 +360,27 @@ def main():
     t_attn_s = comp_ms[1] / 1e3
     achieved = (kv_bytes + qo_bytes) / t_attn_s / 1e9
     kv_gbps = kv_bytes / t_attn_s / 1e9
+    flops = attention_flops(w, n_nodes[0], to_host(base.tree_mask).view(np.uint32))
+    tflops = flops / t_attn_s / 1e12
+    # the dominant kernel's bound: matrix cores above the ridge point
+    mfma_bound = flops / (kv_bytes + qo_bytes) > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    e = 2 if w.dtype == "bf16" else 4
+    logits_gbps = float(n_nodes[0].sum()) * w.V * e / (comp_ms[2] / 1e3) / 1e9
+
+    # a reference streaming read on this GPU: torch's sum over 2 GiB (a
+    # plain reduction kernel; the logits scan of the accept call reads
+    # faster at large batches, so this is a reference, not a ceiling)
+    big = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        big.sum()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(5):
+        big.sum()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stream_gbps = 5 * STREAM_BYTES / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del big
     traffic = measured_traffic(w.name)
     log("next rows: " + ", ".join(f"{k} {v:.1f} us" for k, v in next_us.items()))
     log(f"step {ms_per_step * 1e3:.1f} us (eager {ms_eager * 1e3:.1f}); build {comp_ms[0] * 1e3:.1f} attn "
@@ -371,17 +407,21 @@ def main():
                    "rotating_sets": n_sets},
         "kv_read_GBps": kv_gbps,
         "kv_read_pct_of_peak": 100.0 * kv_gbps / HBM_PEAK_GBPS,
+        "torch_sum_read_GBps": stream_gbps,
+        "logits_scan_GBps": logits_gbps,
+        "attention_TFLOPs": tflops,
         "components_us": {"build": comp_ms[0] * 1e3, "attention": comp_ms[1] * 1e3,
                           "accept": comp_ms[2] * 1e3, "update": comp_ms[3] * 1e3},
         "roofline": {
             "kernel": "graft_tree_attention",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": tflops if mfma_bound else achieved,
+            "peak": MFMA_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": tflops / MFMA_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes + qo_bytes,
+            "algorithmic_flops_per_launch": flops,
             "launch_us": comp_ms[1] * 1e3,
         },
         "cpu_baseline": None,
