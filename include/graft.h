@@ -165,6 +165,11 @@ graft_status graft_build_tree(const graft_tree_config *cfg, int32_t batch,
  *                    ceil(prefix_len/block_size) are never read
  *   prefix_len       int32 [batch], each <= max_prefix (host bound) and
  *                    <= max_blocks_per_seq * block_size
+ *   sum_prefix       host-side sum of prefix_len (<= 0 when unknown): it
+ *                    only steers the launch plan (a ragged batch gets more
+ *                    prefix splits and its longest work launched first);
+ *                    any value gives the same results.  Pass the same value
+ *                    to the workspace query.
  * Arithmetic: fp32 accumulation; bf16 output rounded to nearest even.
  * Supported: block_size 16; head_dim 64 or 128 (bf16 with head_dim 128 takes
  * the matrix-core path when n_nodes * group >= 16 rows).
@@ -172,7 +177,8 @@ graft_status graft_build_tree(const graft_tree_config *cfg, int32_t batch,
  */
 size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch,
                                            int32_t n_max, int32_t hq, int32_t hkv,
-                                           int32_t head_dim, int32_t max_prefix);
+                                           int32_t head_dim, int32_t max_prefix,
+                                           int64_t sum_prefix);
 graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_max,
                                   int32_t hq, int32_t hkv, int32_t head_dim,
                                   const void *q, const void *k_tree,
@@ -181,9 +187,10 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
                                   const int32_t *block_table,
                                   int32_t max_blocks_per_seq,
                                   const int32_t *prefix_len, int32_t max_prefix,
-                                  const uint32_t *tree_mask, const int32_t *n_nodes,
-                                  float scale, void *out, void *workspace,
-                                  size_t workspace_bytes, hipStream_t stream);
+                                  int64_t sum_prefix, const uint32_t *tree_mask,
+                                  const int32_t *n_nodes, float scale, void *out,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * graft_tree_attention_rope -- graft_tree_attention for unrotated queries
@@ -216,8 +223,9 @@ graft_status graft_tree_attention_rope(graft_dtype dtype, int32_t batch, int32_t
                                        const int32_t *block_table,
                                        int32_t max_blocks_per_seq,
                                        const int32_t *prefix_len, int32_t max_prefix,
-                                       const uint32_t *tree_mask, const int32_t *n_nodes,
-                                       const int32_t *tree_pos, const float *rope_cos_sin,
+                                       int64_t sum_prefix, const uint32_t *tree_mask,
+                                       const int32_t *n_nodes, const int32_t *tree_pos,
+                                       const float *rope_cos_sin,
                                        int32_t rope_positions, float scale, void *out,
                                        void *workspace, size_t workspace_bytes,
                                        hipStream_t stream);

@@ -67,9 +67,9 @@ def test_build_tree_validation():
 
 
 def _attn(dtype=1, batch=1, n_max=17, hq=4, hkv=1, D=128, block=16, max_blocks=8,
-          max_prefix=128, ws=None, ws_bytes=0, scale=0.1):
+          max_prefix=128, ws=None, ws_bytes=0, scale=0.1, sum_prefix=0):
     return lib.graft_tree_attention(dtype, batch, n_max, hq, hkv, D, *([FAKE] * 5), block,
-                                    FAKE, max_blocks, FAKE, max_prefix, FAKE, FAKE,
+                                    FAKE, max_blocks, FAKE, max_prefix, sum_prefix, FAKE, FAKE,
                                     ctypes.c_float(scale), FAKE, ws, ws_bytes, None)
 
 
@@ -85,8 +85,11 @@ def test_attention_validation():
     assert _attn(scale=-0.1) == -1
     assert _attn(batch=0) == 0
     # a long prefix needs split partials: no workspace -> workspace error
-    need = lib.graft_tree_attention_workspace_size(1, 1, 61, 32, 8, 128, 65536)
+    need = lib.graft_tree_attention_workspace_size(1, 1, 61, 32, 8, 128, 65536, 0)
     assert need > 0
+    # the prefix-length sum only steers the plan; a ragged batch may split
+    # more, never needs a workspace when nothing is split
+    assert lib.graft_tree_attention_workspace_size(1, 16, 65, 32, 8, 128, 64, 16 * 40) == 0
     assert _attn(n_max=61, hq=32, hkv=8, max_blocks=4096, max_prefix=65536) == -3
     assert "workspace" in G.graft_last_error()
 
@@ -188,7 +191,7 @@ def test_rope_variants_validation():
     def att(**k):
         return lib.graft_tree_attention_rope(
             k.get("dt", 1), k.get("b", 1), k.get("n", 17), 32, 8, k.get("d", 128), *([FAKE] * 5),
-            16, FAKE, 8, FAKE, 128, FAKE, FAKE, k.get("tp", FAKE), k.get("rope", FAKE),
+            16, FAKE, 8, FAKE, 128, 0, FAKE, FAKE, k.get("tp", FAKE), k.get("rope", FAKE),
             k.get("rp", 4096), ctypes.c_float(k.get("scale", 0.088)), FAKE, FAKE, 1 << 24, None)
     assert att(rp=0) == -1
     assert att(tp=None) == -1

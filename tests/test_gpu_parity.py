@@ -277,3 +277,29 @@ def test_update_tree_small_variant(name, over):
     np.testing.assert_array_equal(to_host(ds.m_scores), ref_sc)
     _say(f"[parity] {w.name}: all-node update ok "
          f"({int(ref_tree['n_nodes'].sum())} transitions)")
+
+
+def test_prefix_sum_hint_only_steers_the_plan():
+    """The host-side prefix-length sum picks the launch plan (a ragged batch
+    gets more splits, launched longest first); any value, right or wrong,
+    gives results within the bar."""
+    import torch
+    from tree_attention_verification_graft_amd import binding as G
+    from tree_attention_verification_graft_amd.pipeline import DeviceStep
+    w = W.make("qwen3_8b_b16", B=12, Hq=8, Hkv=2, prefix=(64, 2200), V=1024)
+    ds = DeviceStep(w)
+    ds.build()
+    torch.cuda.synchronize()
+    tree = ds.tree_host()
+    true_sum = int(w.prefix_len.sum())
+    for hint in (0, true_sum, 1, 12 * int(w.max_prefix)):
+        n = G.graft_tree_attention_workspace_size(G.GRAFT_BF16, w.B, ds.n_max, w.Hq, w.Hkv,
+                                                  w.D, w.max_prefix, hint)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+        ds.out.zero_()
+        G.graft_tree_attention(ds.q, ds.k_tree, ds.v_tree, ds.k_cache, ds.v_cache,
+                               ds.block_table, ds.prefix_len, w.max_prefix, ds.tree_mask,
+                               ds.n_nodes, w.scale, ds.out, ws, sum_prefix=hint)
+        torch.cuda.synchronize()
+        err = check_attention(w, ds.out, tree)
+        _say(f"[parity] prefix-sum hint {hint}: attention max-abs {err:.2e}")

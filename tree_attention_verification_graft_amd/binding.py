@@ -79,12 +79,12 @@ def _load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(path)
-    P, I, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    P, I, SZ, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_int64
     sig = {
         "graft_build_tree": [ctypes.POINTER(TreeConfig), I, I, P, P, P, P, P, P, P, I, I,
                              P, P, P, P, P, P, P],
-        "graft_tree_attention_workspace_size": [I, I, I, I, I, I, I],
-        "graft_tree_attention": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, P, P,
+        "graft_tree_attention_workspace_size": [I, I, I, I, I, I, I, I64],
+        "graft_tree_attention": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, I64, P, P,
                                  ctypes.c_float, P, P, SZ, P],
         "graft_accept_workspace_size": [I, I, I],
         "graft_accept": [I, I, I, I, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -96,7 +96,7 @@ def _load(path=LIB_PATH):
         "graft_update_adjacency_tree_workspace_size": [I, I],
         "graft_update_adjacency_tree": [P, P, I, I, I, I, P, P, P, P, SZ, P],
         "graft_append_kv": [I, I, I, I, I, P, P, P, P, I, I, P, I, P, P, P, P, P],
-        "graft_tree_attention_rope": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, P, P,
+        "graft_tree_attention_rope": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, I64, P, P,
                                       P, P, I, ctypes.c_float, P, P, SZ, P],
         "graft_append_kv_rope": [I, I, I, I, I, P, P, P, P, I, I, P, I, P, P, P, P, P, I, P],
         "graft_last_error": [],
@@ -191,14 +191,14 @@ def graft_build_tree(cfg, draft_parent, draft_token, draft_conf, n_draft, root_t
 
 
 def graft_tree_attention_workspace_size(dtype_code, batch, n_max, hq, hkv, head_dim,
-                                        max_prefix):
+                                        max_prefix, sum_prefix=0):
     return int(_lib.graft_tree_attention_workspace_size(dtype_code, batch, n_max, hq, hkv,
-                                                        head_dim, max_prefix))
+                                                        head_dim, max_prefix, int(sum_prefix)))
 
 
 def graft_tree_attention(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
                          max_prefix, tree_mask, n_nodes, scale, out, workspace,
-                         stream=None):
+                         stream=None, sum_prefix=0):
     B, n_max, hq, D = q.shape
     hkv = k_tree.shape[2]
     nblk, _, blk, _ = k_cache.shape
@@ -215,7 +215,8 @@ def graft_tree_attention(q, k_tree, v_tree, k_cache, v_cache, block_table, prefi
     st = _lib.graft_tree_attention(dt, B, n_max, hq, hkv, D, _ptr(q), _ptr(k_tree),
                                    _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), blk,
                                    _ptr(block_table), block_table.shape[1], _ptr(prefix_len),
-                                   int(max_prefix), _ptr(tree_mask), _ptr(n_nodes),
+                                   int(max_prefix), int(sum_prefix), _ptr(tree_mask),
+                                   _ptr(n_nodes),
                                    float(scale), _ptr(out), _ptr(workspace), ws_bytes,
                                    _stream(stream))
     _check(st, "graft_tree_attention")
@@ -223,7 +224,7 @@ def graft_tree_attention(q, k_tree, v_tree, k_cache, v_cache, block_table, prefi
 
 def graft_tree_attention_rope(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
                               max_prefix, tree_mask, n_nodes, tree_pos, rope_cos_sin, scale,
-                              out, workspace, stream=None):
+                              out, workspace, stream=None, sum_prefix=0):
     B, n_max, hq, D = q.shape
     hkv = k_tree.shape[2]
     nblk, _, blk, _ = k_cache.shape
@@ -244,7 +245,8 @@ def graft_tree_attention_rope(q, k_tree, v_tree, k_cache, v_cache, block_table, 
     st = _lib.graft_tree_attention_rope(dt, B, n_max, hq, hkv, D, _ptr(q), _ptr(k_tree),
                                         _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), blk,
                                         _ptr(block_table), block_table.shape[1],
-                                        _ptr(prefix_len), int(max_prefix), _ptr(tree_mask),
+                                        _ptr(prefix_len), int(max_prefix), int(sum_prefix),
+                                        _ptr(tree_mask),
                                         _ptr(n_nodes), _ptr(tree_pos), _ptr(rope_cos_sin),
                                         rope_cos_sin.shape[0], float(scale), _ptr(out),
                                         _ptr(workspace), ws_bytes, _stream(stream))

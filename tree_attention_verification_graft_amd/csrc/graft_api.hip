@@ -160,10 +160,11 @@ static graft_status check_attn_shape(graft_dtype dtype, int32_t batch, int32_t n
 
 size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch, int32_t n_max,
                                            int32_t hq, int32_t hkv, int32_t head_dim,
-                                           int32_t max_prefix) {
+                                           int32_t max_prefix, int64_t sum_prefix) {
   if (check_attn_shape(dtype, batch, n_max, hq, hkv, head_dim, max_prefix) != GRAFT_OK)
     return 0;
-  const AttnPlan pl = plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
+  const AttnPlan pl =
+      plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix, sum_prefix);
   return align_up(pl.part_o_bytes, 256) + align_up(pl.part_ml_bytes, 256);
 }
 
@@ -173,7 +174,8 @@ static graft_status attention_impl(graft_dtype dtype, int32_t batch, int32_t n_m
                                    const void *v_cache, int32_t block_size,
                                    const int32_t *block_table, int32_t max_blocks_per_seq,
                                    const int32_t *prefix_len, int32_t max_prefix,
-                                   const uint32_t *tree_mask, const int32_t *n_nodes,
+                                   int64_t sum_prefix, const uint32_t *tree_mask,
+                                   const int32_t *n_nodes,
                                    const int32_t *tree_pos, const float *rope,
                                    int32_t rope_positions, float scale, void *out,
                                    void *workspace, size_t workspace_bytes,
@@ -193,7 +195,8 @@ static graft_status attention_impl(graft_dtype dtype, int32_t batch, int32_t n_m
               tree_mask && n_nodes && out,
           GRAFT_ERR_INVALID_ARG, "graft_tree_attention: null device pointer");
 
-  const AttnPlan pl = plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
+  const AttnPlan pl =
+      plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix, sum_prefix);
   const size_t need = align_up(pl.part_o_bytes, 256) + align_up(pl.part_ml_bytes, 256);
   REQUIRE(need == 0 || (workspace && workspace_bytes >= need), GRAFT_ERR_WORKSPACE,
           "graft_tree_attention: workspace of %zu bytes needed, %zu given", need,
@@ -226,6 +229,7 @@ static graft_status attention_impl(graft_dtype dtype, int32_t batch, int32_t n_m
   p.tiles_per_split = pl.tiles_per_split;
   p.n_row_groups = pl.n_row_groups;
   p.rows_per_group = pl.rows_per_group;
+  p.lpt = pl.mfma && pl.lpt ? 1 : 0;
   char *ws = static_cast<char *>(workspace);
   p.part_o = pl.n_splits > 1 ? reinterpret_cast<float *>(ws) : nullptr;
   p.part_ml = pl.n_splits > 1
@@ -249,14 +253,16 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
                                   const void *k_cache, const void *v_cache,
                                   int32_t block_size, const int32_t *block_table,
                                   int32_t max_blocks_per_seq, const int32_t *prefix_len,
-                                  int32_t max_prefix, const uint32_t *tree_mask,
-                                  const int32_t *n_nodes, float scale, void *out,
+                                  int32_t max_prefix, int64_t sum_prefix,
+                                  const uint32_t *tree_mask, const int32_t *n_nodes,
+                                  float scale, void *out,
                                   void *workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
   g_error[0] = 0;
   return attention_impl(dtype, batch, n_max, hq, hkv, head_dim, q, k_tree, v_tree, k_cache,
                         v_cache, block_size, block_table, max_blocks_per_seq, prefix_len,
-                        max_prefix, tree_mask, n_nodes, nullptr, nullptr, 0, scale, out,
+                        max_prefix, sum_prefix, tree_mask, n_nodes, nullptr, nullptr, 0, scale,
+                        out,
                         workspace, workspace_bytes, stream);
 }
 
@@ -266,8 +272,9 @@ graft_status graft_tree_attention_rope(graft_dtype dtype, int32_t batch, int32_t
                                        const void *k_cache, const void *v_cache,
                                        int32_t block_size, const int32_t *block_table,
                                        int32_t max_blocks_per_seq, const int32_t *prefix_len,
-                                       int32_t max_prefix, const uint32_t *tree_mask,
-                                       const int32_t *n_nodes, const int32_t *tree_pos,
+                                       int32_t max_prefix, int64_t sum_prefix,
+                                       const uint32_t *tree_mask, const int32_t *n_nodes,
+                                       const int32_t *tree_pos,
                                        const float *rope_cos_sin, int32_t rope_positions,
                                        float scale, void *out, void *workspace,
                                        size_t workspace_bytes, hipStream_t stream) {
@@ -280,7 +287,8 @@ graft_status graft_tree_attention_rope(graft_dtype dtype, int32_t batch, int32_t
           "graft_tree_attention_rope: the table must be 16-byte aligned");
   return attention_impl(dtype, batch, n_max, hq, hkv, head_dim, q, k_tree, v_tree, k_cache,
                         v_cache, block_size, block_table, max_blocks_per_seq, prefix_len,
-                        max_prefix, tree_mask, n_nodes, tree_pos, rope_cos_sin, rope_positions,
+                        max_prefix, sum_prefix, tree_mask, n_nodes, tree_pos, rope_cos_sin,
+                        rope_positions,
                         scale, out, workspace, workspace_bytes, stream);
 }
 

@@ -65,16 +65,20 @@ struct AttnParams {
   int32_t tiles_per_split; // 64-key prefix tiles per split
   int32_t n_row_groups;    // row groups per (sequence, kv head)
   int32_t rows_per_group;  // query rows per group (multiple of 16)
+  int32_t lpt;             // rank (sequence, split) pairs longest first on the device
   float *part_o;           // [batch][hkv][groups][splits][rows][D]
   float *part_ml;          // [batch][hkv][groups][splits][rows][2]
 };
 struct AttnPlan {
   bool mfma;
+  bool lpt;  // ragged batch: launch the longest (sequence, split) work first
   int32_t n_splits, tiles_per_split, n_row_groups, rows_per_group;
   size_t part_o_bytes, part_ml_bytes;
 };
+// sum_prefix: the caller's sum of prefix lengths (<= 0: unknown, every
+// sequence is taken at max_prefix); it only steers the plan.
 AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hq,
-                        int32_t hkv, int32_t head_dim, int32_t max_prefix);
+                        int32_t hkv, int32_t head_dim, int32_t max_prefix, int64_t sum_prefix);
 void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream);
 void launch_attention_wave(graft_dtype dtype, const AttnParams &p, hipStream_t stream);
 void launch_attention_combine(graft_dtype dtype, const AttnParams &p,

@@ -657,7 +657,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   }
 }
 
-template <int NB, bool ROPE>
+template <int NB, bool ROPE, bool LPT>
 __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   __shared__ int32_t s_tpos[ROPE ? GRAFT_MAX_NODES : 1];  // tree positions (rotary path)
@@ -673,9 +673,44 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
     const int cluster = (slot / p.n_row_groups) * 8 + xcd;
     const int n_clusters = p.batch * p.hkv * p.n_splits;
     if (cluster >= n_clusters) return;
-    c.split = cluster % p.n_splits;
-    c.h = (cluster / p.n_splits) % p.hkv;
-    c.b = cluster / (p.n_splits * p.hkv);
+    if (LPT) {
+      // Longest first: (sequence, split) pairs ranked by their tile count
+      // (the tree tiles counted in split 0), descending, ties by pair index;
+      // cluster k takes the pair of rank k / hkv and KV head k % hkv, so the
+      // dispatcher starts the longest work first whatever the prefix lengths.
+      __shared__ int32_t s_w[kMfmaThreads];
+      __shared__ int32_t s_pair;
+      const int t = threadIdx.x, S = p.n_splits;
+      const int n_pairs = p.batch * S;  // <= kMfmaThreads (host check)
+      int w = -1;
+      if (t < n_pairs) {
+        const int b = t / S, sp = t % S;
+        const int P = min(max(p.prefix_len[b], 0), p.max_blocks * kBlock);
+        const int tiles = (P + kTile - 1) / kTile;
+        w = max(0, min(p.tiles_per_split, tiles - sp * p.tiles_per_split));
+        if (sp == 0) w += (min(max(p.n_nodes[b], 0), p.n_max) + kTile - 1) / kTile;
+        s_w[t] = w;
+      }
+      __syncthreads();
+      const int q = cluster / p.hkv;
+      if (t < n_pairs) {
+        int rank = 0;
+        for (int u = 0; u < n_pairs; ++u) {
+          const int wu = s_w[u];
+          rank += (wu > w || (wu == w && u < t)) ? 1 : 0;
+        }
+        if (rank == q) s_pair = t;
+      }
+      __syncthreads();
+      const int pair = s_pair;
+      c.split = pair % S;
+      c.b = pair / S;
+      c.h = cluster % p.hkv;
+    } else {
+      c.split = cluster % p.n_splits;
+      c.h = (cluster / p.n_splits) % p.hkv;
+      c.b = cluster / (p.n_splits * p.hkv);
+    }
   }
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
@@ -1024,7 +1059,7 @@ int busiest_simd_blocks(int blocks_per_group) {
 }  // namespace
 
 AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hq,
-                        int32_t hkv, int32_t head_dim, int32_t max_prefix) {
+                        int32_t hkv, int32_t head_dim, int32_t max_prefix, int64_t sum_prefix) {
   AttnPlan pl{};
   const int group = hq / hkv;
   const int rows = n_max * group;
@@ -1034,24 +1069,64 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
     const int blocks = (rows + 15) / 16;
     const int per_group = kMfmaWaves * kMaxNB;
     const int g_min = (blocks + per_group - 1) / per_group;
-    const double kv_bytes = (double)batch * hkv * tiles * kTile * kD * 2 * 2;
+    // Modelled prefix lengths: every sequence at max_prefix, unless the
+    // caller's sum says the batch is ragged; then M representative lengths
+    // spread evenly around the mean up to the maximum (each standing for
+    // batch / M sequences).
+    // (the device ranks batch x splits pairs in one workgroup pass, so a
+    // ragged plan needs batch <= kMfmaThreads)
+    const bool ragged = batch > 1 && batch <= kMfmaThreads && sum_prefix > 0 &&
+                        sum_prefix < (int64_t)batch * max_prefix;
+    const int M = ragged ? min(batch, 64) : 1;
+    const double mult = (double)batch / M;
+    double len[64];
+    {
+      const double mean = ragged ? (double)sum_prefix / batch : (double)max_prefix;
+      const double hi = ragged ? std::min((double)max_prefix, 2.0 * mean) : (double)max_prefix;
+      const double lo = ragged ? std::max(0.0, 2.0 * mean - hi) : hi;
+      for (int i = 0; i < M; ++i) len[i] = lo + (hi - lo) * (i + 0.5) / M;
+    }
+    pl.lpt = ragged;
+    const int tree_tiles = (n_max + kTile - 1) / kTile;
     double best = 1e30;
     for (int groups = g_min; groups <= min(blocks, 4 * g_min); ++groups) {
       const int bpg = (blocks + groups - 1) / groups;
       const int simd = busiest_simd_blocks(bpg);
+      const double tile_us = kTileFixedUs + simd * kTileBlockUs;
       for (int splits = 1; splits <= min(tiles, kMaxSplits); ++splits) {
         const int tps = (tiles + splits - 1) / splits;
         const int eff_splits = (tiles + tps - 1) / tps;
         if (eff_splits != splits) continue;
-        const long wgs = (long)batch * hkv * groups * splits;
-        const long rounds = (wgs + kComputeUnits - 1) / kComputeUnits;
-        const double t_tiles = rounds * tps * (kTileFixedUs + simd * kTileBlockUs);
+        if (ragged && (long)batch * splits > kMfmaThreads) continue;  // device ranking
+        // workgroups per modelled sequence, their total time and the longest
+        double n_wg = 0, total_us = 0, longest_us = 0, kv_bytes = 0, active = 0;
+        for (int i = 0; i < M; ++i) {
+          const int t_i = (int)((len[i] + kTile - 1) / kTile);
+          const int s_i = max(1, (t_i + tps - 1) / tps);
+          const double wgs_i = mult * hkv * groups * s_i;
+          n_wg += wgs_i;
+          total_us += mult * hkv * groups * ((t_i + tree_tiles) * tile_us + s_i * kRoundUs);
+          longest_us = std::max(longest_us, (std::min(tps, t_i) + tree_tiles) * tile_us + kRoundUs);
+          kv_bytes += mult * hkv * (double)t_i * kTile * kD * 2 * 2;
+          active += mult * s_i;
+        }
+        // one workgroup per compute unit at a time: with every workgroup
+        // equal this is rounds x (tps tiles + overhead); ragged batches run
+        // longest first, which packs to about total / CUs, never below the
+        // longest workgroup
         const double t_l2 = groups * kv_bytes / kL2BytesPerUs;
         const double t_hbm = kv_bytes / kHbmBytesPerUs;
-        double t = std::max(t_tiles, std::max(t_l2, t_hbm)) + rounds * kRoundUs;
+        double t;
+        if (!ragged) {
+          const long rounds = (long)((n_wg + kComputeUnits - 1) / kComputeUnits);
+          t = std::max(rounds * tps * tile_us, std::max(t_l2, t_hbm)) + rounds * kRoundUs;
+        } else {
+          const double t_tiles =
+              std::max(longest_us, total_us / kComputeUnits + 0.5 * total_us / n_wg);
+          t = std::max(t_tiles, std::max(t_l2, t_hbm));
+        }
         if (splits > 1)
-          t += kCombineUs + (double)batch * n_max * hq * splits * (head_dim + 2) * 4.0 * 2.0 /
-                                kPartialBytesPerUs;
+          t += kCombineUs + active * n_max * hq * (head_dim + 2) * 4.0 * 2.0 / kPartialBytesPerUs;
         if (t < best) {
           best = t;
           pl.n_row_groups = groups;
@@ -1076,23 +1151,27 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
   return pl;
 }
 
+namespace {
+template <int NB>
+void launch_mfma(const AttnParams &p, dim3 grid, hipStream_t stream) {
+  const int kind = (p.rope ? 1 : 0) + (p.lpt ? 2 : 0);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, false>), grid, dim3(kMfmaThreads), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, false>), grid, dim3(kMfmaThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, true>), grid, dim3(kMfmaThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, true>), grid, dim3(kMfmaThreads), 0, stream, p); break;
+  }
+}
+}  // namespace
+
 void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream) {
   const long clusters = (long)p.batch * p.hkv * p.n_splits;
   dim3 grid((unsigned)(8 * p.n_row_groups * ((clusters + 7) / 8)));
   const int nb = (p.rows_per_group / 16 + kMfmaWaves - 1) / kMfmaWaves;
   switch (nb) {
-    case 1:
-      if (p.rope) hipLaunchKernelGGL((attn_mfma_kernel<1, true>), grid, dim3(kMfmaThreads), 0, stream, p);
-      else hipLaunchKernelGGL((attn_mfma_kernel<1, false>), grid, dim3(kMfmaThreads), 0, stream, p);
-      break;
-    case 2:
-      if (p.rope) hipLaunchKernelGGL((attn_mfma_kernel<2, true>), grid, dim3(kMfmaThreads), 0, stream, p);
-      else hipLaunchKernelGGL((attn_mfma_kernel<2, false>), grid, dim3(kMfmaThreads), 0, stream, p);
-      break;
-    default:
-      if (p.rope) hipLaunchKernelGGL((attn_mfma_kernel<3, true>), grid, dim3(kMfmaThreads), 0, stream, p);
-      else hipLaunchKernelGGL((attn_mfma_kernel<3, false>), grid, dim3(kMfmaThreads), 0, stream, p);
-      break;
+    case 1: launch_mfma<1>(p, grid, stream); break;
+    case 2: launch_mfma<2>(p, grid, stream); break;
+    default: launch_mfma<3>(p, grid, stream); break;
   }
 }
 

@@ -72,8 +72,10 @@ class DeviceStep:
         self.new_prefix_len = torch.empty((B,), dtype=i32, device=d)
         # workspaces
         dt = G.GRAFT_BF16 if w.dtype == "bf16" else G.GRAFT_F32
+        # the host-side sum of the prefix lengths steers the attention plan
+        self.sum_prefix = int(np.asarray(w.prefix_len, np.int64).sum())
         n = G.graft_tree_attention_workspace_size(dt, B, self.n_max, w.Hq, w.Hkv, w.D,
-                                                  w.max_prefix)
+                                                  w.max_prefix, self.sum_prefix)
         self.attn_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=d)
         n = G.graft_accept_workspace_size(B, self.n_max, w.V)
         self.accept_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=d)
@@ -100,7 +102,7 @@ class DeviceStep:
         G.graft_tree_attention(self.q, self.k_tree, self.v_tree, self.k_cache, self.v_cache,
                                self.block_table, self.prefix_len, self.w.max_prefix,
                                self.tree_mask, self.n_nodes, self.w.scale, self.out,
-                               self.attn_ws)
+                               self.attn_ws, sum_prefix=self.sum_prefix)
 
     def accept(self):
         G.graft_accept(self.logits, self.tree_token, self.tree_parent, self.tree_mask,
@@ -134,7 +136,8 @@ class DeviceStep:
         G.graft_tree_attention_rope(self.q, self.k_tree, self.v_tree, self.k_cache, self.v_cache,
                                     self.block_table, self.prefix_len, self.w.max_prefix,
                                     self.tree_mask, self.n_nodes, self.tree_pos, self.rope,
-                                    self.w.scale, self.out, self.attn_ws)
+                                    self.w.scale, self.out, self.attn_ws,
+                                    sum_prefix=self.sum_prefix)
 
     def append_rope(self):
         G.graft_append_kv_rope(self.k_tree, self.v_tree, self.k_cache, self.v_cache,
