@@ -28,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -127,9 +128,11 @@ def traffic_from_pmc(name, fetch_dir, write_dir):
         kib_calib = calib[0][0]
         factor = kib_calib * 1024.0 / CALIBRATION_BYTES
         # the plain call's kernels (the fused-RoPE instantiations of the same
-        # templates are timed beside the step, not here)
+        # template, attn_mfma_kernel<NB, true, ...>, are timed beside the
+        # step, not here)
         call_kib = sum(v[0] for k, v in means.items()
-                       if any(a in k for a in ATTN_KERNELS) and ", true>" not in k)
+                       if any(a in k for a in ATTN_KERNELS)
+                       and not re.search(r"attn_mfma_kernel<\d+, true", k))
         out[counter] = {"calibration_kib": kib_calib, "factor": factor,
                         "attention_call_kib": call_kib,
                         "bytes_per_call": call_kib * 1024.0 / factor}
