@@ -224,8 +224,6 @@ template <int NA, bool ROPE>
 __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
                                                uint8_t *smem, int32_t *s_tpos) {
   constexpr int NQ = NA > 0 ? NA : 1;
-  // V operands read ahead of the softmax (all eight where registers allow)
-  constexpr int kVPre = NA >= 2 ? 4 : 8;
   const __bf16 *q = static_cast<const __bf16 *>(p.q);
   const __bf16 *k_cache = static_cast<const __bf16 *>(p.k_cache);
   const __bf16 *v_cache = static_cast<const __bf16 *>(p.v_cache);
@@ -378,29 +376,21 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
                                                                 sc[k][hh], 0, 0, 0);
     }
   };
-  auto sm_pv_half = [&](int st, int kp, int key0, bool tree, f32x4 (&sc)[NQ][2]) {
-    const uint8_t *sV = smem + st * kStageBytes + kKBytes + kp * 8192 + v_off;
-    // the first kVPre V operands are read before the softmax
-    bf16x8 va[kVPre];
-#pragma unroll
-    for (int d = 0; d < kVPre; ++d) va[d] = *reinterpret_cast<const bf16x8 *>(sV + d * 512);
+  // Softmax of one half in three pieces, so that a half's vector work can
+  // sit beside the other half's matrix ops in one basic block:
+  //  - prep_half masks the scores where needed and returns, as a
+  //    wave-uniform bit set, the blocks whose exponent offset must move
+  //    (their lane maxima are left in mx);
+  //  - rescale_half moves those offsets (the rare branch);
+  //  - exp_half turns the scores into bf16 probabilities.
+  auto prep_half = [&](int kp, int key0, bool tree, f32x4 (&sc)[NQ][2], float (&mx)[NQ]) {
     const int limit = tree ? c.n_nodes : c.P;
     const bool masked = tree || key0 + kTile > c.P;  // wave-uniform
-    bf16x8 pb[NQ];
+    uint32_t rs = 0;
 #pragma unroll
     for (int k = 0; k < NA; ++k) {
       f32x4(&s)[2] = sc[k];
-      bool rescale;
-      float mx;
-      if (!masked) {
-        // Common case: the lane's own maximum of its 8 raw scores against
-        // the raw-score threshold of the lazy rescale; the exact maximum
-        // over the half (across the four lane groups) is only needed when
-        // some score crosses it.
-        mx = max8(s[0], s[1], pinf);
-        rescale = __ballot(mx > thr_raw[k]) != 0ull;
-        if (rescale) mx = group4_max(mx, pinf);
-      } else {
+      if (masked) {
         const uint32_t(&mw)[4] = tmask[k];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -411,12 +401,21 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
             if (tree) vis = vis && ((mask_word(mw, key >> 5) >> (key & 31)) & 1u);
             s[hh][i] = vis ? s[hh][i] : -INFINITY;
           }
-        mx = group4_max(max8(s[0], s[1], pinf), pinf);
-        rescale = __ballot(mx * p.scale_log2 > m_run[k] + kRescaleLog2) != 0ull;
       }
-      if (rescale) {
+      // the lane's maximum of its 8 raw scores against the raw-score
+      // threshold of the lazy rescale; the maximum over the half (across
+      // the four lane groups) is only needed when some score crosses it
+      mx[k] = max8(s[0], s[1], pinf);
+      if (__ballot(mx[k] > thr_raw[k]) != 0ull) rs |= 1u << k;
+    }
+    return rs;
+  };
+  auto rescale_half = [&](const float (&mx)[NQ], uint32_t rs) {
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
+      if (rs & (1u << k)) {
         // new offset: the half's maximum (in log2 units) if it is larger
-        const float m_new = fmaxf(m_run[k], mx * p.scale_log2);
+        const float m_new = fmaxf(m_run[k], group4_max(mx[k], pinf) * p.scale_log2);
         const float alpha = fast_exp2(m_run[k] - m_new);
         m_run[k] = m_new;
         thr_raw[k] = (m_new + kRescaleLog2) * inv_scale_log2;
@@ -424,38 +423,70 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
 #pragma unroll
         for (int d = 0; d < 8; ++d) o[k][d] *= alpha;
       }
+    }
+  };
+  auto exp_half = [&](const f32x4 (&sc)[NQ][2], bf16x8 (&pb)[NQ]) {
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
       const float neg_m = -m_run[k];
       bf16x8 v;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          v[4 * hh + i] = (__bf16)fast_exp2(fmaf(s[hh][i], p.scale_log2, neg_m));
+          v[4 * hh + i] = (__bf16)fast_exp2(fmaf(sc[k][hh][i], p.scale_log2, neg_m));
       pb[k] = v;
     }
-    if (NA > 0) {
-      bf16x8 ones;
+  };
+  // P V ops of half kp (and the row-sum op against a ones operand).
+  auto pv_half = [&](int st, int kp, const bf16x8 (&pb)[NQ]) {
+    const uint8_t *sV = smem + st * kStageBytes + kKBytes + kp * 8192 + v_off;
+    bf16x8 ones;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
+#pragma unroll
+    for (int k = 0; k < NA; ++k)
+      l_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], l_acc[k], 0, 0, 0);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sV + d * 512);
 #pragma unroll
       for (int k = 0; k < NA; ++k)
-        l_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], l_acc[k], 0, 0, 0);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const bf16x8 av = d < kVPre ? va[d < kVPre ? d : 0]
-                                    : *reinterpret_cast<const bf16x8 *>(sV + d * 512);
-#pragma unroll
-        for (int k = 0; k < NA; ++k)
-          o[k][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[k], o[k][d], 0, 0, 0);
-      }
+        o[k][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[k], o[k][d], 0, 0, 0);
     }
   };
+  // One 64-key tile.  Up to two blocks per wave it is software-pipelined
+  // over its two halves: the first half's exponentials share a basic block
+  // with the second half's score ops, and the first half's P V ops with the
+  // second half's masking and maxima, so that each wave keeps its matrix
+  // cores busy through much of its own softmax.  Three blocks do not leave
+  // the registers for two halves of scores, so there the halves run one
+  // after the other.
   auto compute = [&](int st, int key0, bool tree) {
+    if constexpr (NA <= 2) {
+      f32x4 sa[NQ][2], sb[NQ][2];
+      float ma[NQ], mb[NQ];
+      bf16x8 pa[NQ], pz[NQ];
+      qk_half(st, 0, sa);
+      rescale_half(ma, prep_half(0, key0, tree, sa, ma));
+      exp_half(sa, pa);
+      qk_half(st, 1, sb);
+      pv_half(st, 0, pa);
+      const uint32_t rb = prep_half(1, key0, tree, sb, mb);
+      rescale_half(mb, rb);
+      exp_half(sb, pz);
+      pv_half(st, 1, pz);
+    } else {
 #pragma unroll 1
-    for (int kp = 0; kp < 2; ++kp) {
-      f32x4 sc[NQ][2];
-      qk_half(st, kp, sc);
-      sm_pv_half(st, kp, key0, tree, sc);
+      for (int kp = 0; kp < 2; ++kp) {
+        f32x4 sc[NQ][2];
+        float mx[NQ];
+        bf16x8 pb[NQ];
+        qk_half(st, kp, sc);
+        rescale_half(mx, prep_half(kp, key0, tree, sc, mx));
+        exp_half(sc, pb);
+        pv_half(st, kp, pb);
+      }
     }
   };
 
@@ -1031,7 +1062,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 // ring and registers fill one), so the plan picks the number of row groups
 // and prefix splits that minimise an estimate of the kernel's time:
 //   rounds * tiles per workgroup * (a per-tile cost + a cost per 16-row
-//   block on the busiest SIMD)
+//   block on the busiest SIMD + a cost per block of the workgroup)
 // bounded below by the HBM and L2 streams, plus a fixed cost per round
 // (dispatch, prologue, epilogue) and, when the prefix is split, the combine
 // launch and the split partials' traffic.  The constants are measured on
@@ -1039,8 +1070,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 // workgroups per compute unit.
 namespace {
 constexpr int kComputeUnits = 256;
-constexpr double kTileFixedUs = 0.6;          // per 64-key tile, any block count
-constexpr double kTileBlockUs = 0.4;          // per 16-row block on the busiest SIMD
+constexpr double kTileFixedUs = 0.4;          // per 64-key tile, any block count
+constexpr double kTileBlockUs = 0.15;         // per 16-row block on the busiest SIMD
+constexpr double kTileGroupBlockUs = 0.07;    // per 16-row block of the workgroup
 constexpr double kRoundUs = 6.0;              // dispatch + prologue + epilogue
 constexpr double kCombineUs = 4.0;            // combine launch
 constexpr double kPartialBytesPerUs = 5.0e6;  // partials written, then read back
@@ -1092,7 +1124,7 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
     for (int groups = g_min; groups <= min(blocks, 4 * g_min); ++groups) {
       const int bpg = (blocks + groups - 1) / groups;
       const int simd = busiest_simd_blocks(bpg);
-      const double tile_us = kTileFixedUs + simd * kTileBlockUs;
+      const double tile_us = kTileFixedUs + simd * kTileBlockUs + bpg * kTileGroupBlockUs;
       for (int splits = 1; splits <= min(tiles, kMaxSplits); ++splits) {
         const int tps = (tiles + splits - 1) / splits;
         const int eff_splits = (tiles + tps - 1) / tps;
