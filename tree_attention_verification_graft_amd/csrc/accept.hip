@@ -27,6 +27,7 @@ namespace graft {
 namespace {
 
 constexpr int kThreads = 256;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSmallLoads = 2;      // 16-byte loads per thread, small grids
 constexpr int kLargeLoads = 8;      // ... large grids
 constexpr int kLargeGrid = 8192;    // workgroups above which chunks grow
@@ -81,7 +82,13 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(AcceptParams p)
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int e = lo + (k * kThreads + threadIdx.x) * kPer;
-      v[k] = e < hi ? x[e / kPer] : make_uint4(0u, 0u, 0u, 0u);
+      // read once: non-temporal loads stream past the caches
+      if (e < hi) {
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x) + e / kPer);
+        v[k] = make_uint4(t.x, t.y, t.z, t.w);
+      } else {
+        v[k] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {

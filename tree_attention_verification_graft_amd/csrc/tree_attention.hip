@@ -169,12 +169,22 @@ constexpr int kDmaPerStage = 4;          // per wave: 2 K + 2 V instructions
 
 // Issue one asynchronous 16-byte-per-lane global->LDS load from
 // base + voffset (base wave-uniform, in SGPRs).  lds_base is the
-// wave-uniform LDS byte address of the 1 KB destination block.
+// wave-uniform LDS byte address of the 1 KB destination block.  The
+// non-temporal form is for tiles no other workgroup reads again.
 __device__ __forceinline__ void dma16(const void *base, uint32_t voffset, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_base), "v"(voffset), "s"(base)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt(const void *base, uint32_t voffset, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt"
       :
       : "s"(lds_base), "v"(voffset), "s"(base)
       : "memory", "m0");
@@ -328,11 +338,20 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   auto tile_page = [&](int it) {
     return table[(uint32_t)min((c.t_begin + it) * 4 + my_page, last_page)];
   };
+  // With one row group no other workgroup reads a tile again, so the tiles
+  // stream past the caches; several row groups re-read each other's tiles
+  // through L2.
+  const bool read_once = p.n_row_groups == 1;
   auto issue_prefix = [&](int st, int blk) {
     const char *base = kv_base + (uint64_t)(uint32_t)blk * page_stride;
     const uint32_t sbase = c.lds0 + st * kStageBytes;
+    if (read_once) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(base, dma_off[q], sbase + dma_dst(q));
+      for (int q = 0; q < 4; ++q) dma16_nt(base, dma_off[q], sbase + dma_dst(q));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma16(base, dma_off[q], sbase + dma_dst(q));
+    }
   };
 
   // ancestor masks of the wave's rows (read before the tree tiles)
