@@ -215,6 +215,10 @@ __device__ inline int v_lds_offset(int d, int key) {
 struct MfmaCtx {
   int b, h, rg, split, tid, lane, n16, g4, wave;
   int n_nodes, P, G, rows_b, row0, n_pages_b, t_begin, n_pref, n_tree;
+  // Row blocks of the wave: rows row0 + 16 * (wslot + wstride * k).  With
+  // key pairs, waves w and w + 4 own the same blocks (wslot = w & 3,
+  // wstride 4) and each takes one 32-key half (khalf) of every tile.
+  int wslot, wstride, khalf;
   uint32_t lds0;  // LDS byte address of stage 0
   // The wave's page-table entries for the split's first three tiles and the
   // sequence's first page, loaded before the prefix length is known (indices
@@ -230,7 +234,7 @@ struct MfmaCtx {
 // One wave's share, specialised on the number NA of 16-row query blocks it
 // owns (wave-uniform), so that no matrix instruction sits behind a per-block
 // branch.  Every wave runs the same loads and barriers whatever NA is.
-template <int NA, bool ROPE>
+template <int NA, bool ROPE, bool PAIR>
 __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
                                                uint8_t *smem, int32_t *s_tpos) {
   constexpr int NQ = NA > 0 ? NA : 1;
@@ -252,7 +256,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   float thr_raw[NQ];
   const float inv_scale_log2 = 1.f / p.scale_log2;
   const float pinf = pos_inf();
-  auto row_of = [&](int k) { return c.row0 + 16 * (wave + kMfmaWaves * k) + n16; };
+  auto row_of = [&](int k) { return c.row0 + 16 * (c.wslot + c.wstride * k) + n16; };
 #pragma unroll
   for (int k = 0; k < NA; ++k) {
     const int r = row_of(k);
@@ -482,7 +486,15 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   // the registers for two halves of scores, so there the halves run one
   // after the other.
   auto compute = [&](int st, int key0, bool tree) {
-    if constexpr (NA <= 2) {
+    if constexpr (PAIR) {
+      f32x4 sc[NQ][2];
+      float mx[NQ];
+      bf16x8 pb[NQ];
+      qk_half(st, c.khalf, sc);
+      rescale_half(mx, prep_half(c.khalf, key0, tree, sc, mx));
+      exp_half(sc, pb);
+      pv_half(st, c.khalf, pb);
+    } else if constexpr (NA <= 2) {
       f32x4 sa[NQ][2], sb[NQ][2];
       float ma[NQ], mb[NQ];
       bf16x8 pa[NQ], pz[NQ];
@@ -668,6 +680,38 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     if (NA > 0) compute(0, key0, true);
   }
 
+  // ---- key pairs: the wave of the second half hands its (O, max, sum)
+  // to its partner through LDS (the stage ring is free once every wave is
+  // past its last tile), and the partner merges them by log-sum-exp.
+  if constexpr (PAIR) {
+    lds_barrier();
+    f32x4 *xo = reinterpret_cast<f32x4 *>(smem);  // [slot][k][d][lane]
+    float *xml = reinterpret_cast<float *>(smem + 4 * NQ * 8 * 64 * 16);  // [slot][k][lane][2]
+    if (c.khalf == 1) {
+#pragma unroll
+      for (int k = 0; k < NA; ++k) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) xo[((c.wslot * NQ + k) * 8 + d) * 64 + lane] = o[k][d];
+        xml[((c.wslot * NQ + k) * 64 + lane) * 2 + 0] = m_run[k];
+        xml[((c.wslot * NQ + k) * 64 + lane) * 2 + 1] = l_acc[k][0];
+      }
+    }
+    lds_barrier();
+    if (c.khalf == 1) return;
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
+      const float mb = xml[((c.wslot * NQ + k) * 64 + lane) * 2 + 0];
+      const float lb = xml[((c.wslot * NQ + k) * 64 + lane) * 2 + 1];
+      const float mm = fmaxf(m_run[k], mb);
+      const float fa = fast_exp2(m_run[k] - mm), fb = fast_exp2(mb - mm);
+      m_run[k] = mm;
+      l_acc[k][0] = l_acc[k][0] * fa + lb * fb;
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        o[k][d] = o[k][d] * fa + xo[((c.wslot * NQ + k) * 8 + d) * 64 + lane] * fb;
+    }
+  }
+
   // ---- epilogue: finish the row sums across the four lane groups and
   // write either the output or this split's partials.
 #pragma unroll
@@ -765,12 +809,16 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  const bool pair = NB == 1 && p.key_pairs;
+  c.wslot = pair ? (c.wave & 3) : c.wave;
+  c.wstride = pair ? 4 : kMfmaWaves;
+  c.khalf = pair ? (c.wave >> 2) : 0;
   if (ROPE) {
     // before the node count is known: indices clamped to the row
     const int32_t *tp = p.tree_pos + (size_t)c.b * p.n_max;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int r = c.rg * p.rows_per_group + 16 * (c.wave + kMfmaWaves * k) + (c.lane & 15);
+      const int r = c.rg * p.rows_per_group + 16 * (c.wslot + c.wstride * k) + (c.lane & 15);
       c.qpos[k] = tp[min(r / p.group, p.n_max - 1)];
     }
     c.tpos = c.tid < p.n_max ? tp[c.tid] : 0;
@@ -810,13 +858,19 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   int na = 0;
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    const int rl = 16 * (c.wave + kMfmaWaves * k);
+    const int rl = 16 * (c.wslot + c.wstride * k);
     if (rl < p.rows_per_group && c.row0 + rl < c.rows_b) na = k + 1;
   }
-  if (NB >= 3 && na == 3) mfma_wave_body<3, ROPE>(p, c, smem, s_tpos);
-  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1), ROPE>(p, c, smem, s_tpos);
-  else if (na == 1) mfma_wave_body<1, ROPE>(p, c, smem, s_tpos);
-  else mfma_wave_body<0, ROPE>(p, c, smem, s_tpos);
+  if (NB >= 3 && na == 3) mfma_wave_body<3, ROPE, false>(p, c, smem, s_tpos);
+  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1), ROPE, false>(p, c, smem, s_tpos);
+  else if (na == 1) {
+    if (pair) mfma_wave_body<1, ROPE, true>(p, c, smem, s_tpos);
+    else mfma_wave_body<1, ROPE, false>(p, c, smem, s_tpos);
+  } else if (pair) {
+    mfma_wave_body<0, ROPE, true>(p, c, smem, s_tpos);
+  } else {
+    mfma_wave_body<0, ROPE, false>(p, c, smem, s_tpos);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -1142,7 +1196,9 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
     double best = 1e30;
     for (int groups = g_min; groups <= min(blocks, 4 * g_min); ++groups) {
       const int bpg = (blocks + groups - 1) / groups;
-      const int simd = busiest_simd_blocks(bpg);
+      // up to 4 blocks: key pairs, each SIMD's two waves on half the keys
+      const bool pairs = bpg <= 4;
+      const double simd = pairs ? 0.5 : busiest_simd_blocks(bpg);
       const double tile_us = kTileFixedUs + simd * kTileBlockUs + bpg * kTileGroupBlockUs;
       for (int splits = 1; splits <= min(tiles, kMaxSplits); ++splits) {
         const int tps = (tiles + splits - 1) / splits;
@@ -1184,6 +1240,7 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
           pl.rows_per_group = 16 * bpg;
           pl.tiles_per_split = tps;
           pl.n_splits = splits;
+          pl.key_pairs = pairs;
         }
       }
     }
