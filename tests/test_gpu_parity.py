@@ -153,6 +153,9 @@ EDGE = [
                                       n_draft=256, prefix_list=[90, 1000], V=3000)),
     # vocab not a multiple of 8 (scalar argmax loads), fp32 head dim 128
     ("odd_vocab_f32", "tiny_f32", dict(D=128, V=999, prefix=(77, 77))),
+    # a long prefix over one KV head: more than 32 prefix splits to combine
+    ("many_splits", "llama3_8b_b1", dict(B=1, Hq=4, Hkv=1, kmax=16, stage_k_ret=[8, 4, 0],
+                                         n_draft=16, prefix_list=[20000], V=2048)),
     # GQA group 16 with several row groups and a split prefix
     ("group16_long", "qwen3_235b_share", dict(B=2, Hq=32, Hkv=2, prefix_list=[2500, 4100],
                                               V=3000)),
