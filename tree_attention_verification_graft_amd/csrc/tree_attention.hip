@@ -347,7 +347,15 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   // through L2.
   const bool read_once = p.n_row_groups == 1;
   auto issue_prefix = [&](int st, int blk) {
-    const char *base = kv_base + (uint64_t)(uint32_t)blk * page_stride;
+    // the page base is wave-uniform; read it from lane 0 so that it stays in
+    // SGPRs for the asm operand whatever the register pressure around it
+    const uint64_t ba = (uint64_t)(uintptr_t)(kv_base + (uint64_t)(uint32_t)blk * page_stride);
+    // (readfirstlane returns int: each half goes through uint32_t so that
+    // the low half is zero-extended, never sign-extended into the high one)
+    const uint32_t ba_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ba >> 32));
+    const uint32_t ba_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ba);
+    const char *base =
+        reinterpret_cast<const char *>(((uint64_t)ba_hi << 32) | (uint64_t)ba_lo);
     const uint32_t sbase = c.lds0 + st * kStageBytes;
     if (read_once) {
 #pragma unroll
@@ -535,6 +543,52 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   if (c.n_pref > 0) issue_prefix(0, fix_page(c.pre_page[0], 0));
   if (c.n_pref > 1) issue_prefix(1, fix_page(c.pre_page[1], 1));
   if (c.n_pref > 2) page_next = fix_page(c.pre_page[2], 2);
+  // Waves with at most one block have the registers to hold the first tree
+  // tile (keys 0..63) and their ancestor masks from here on, so its loads
+  // go out with the queries instead of one global round trip before the
+  // tree tile (the workgroups of split 0 end last by that much otherwise).
+  constexpr bool kTreePre = NA <= 1 && !ROPE;
+  const __bf16 *k_tree = static_cast<const __bf16 *>(p.k_tree);
+  const __bf16 *v_tree = static_cast<const __bf16 *>(p.v_tree);
+  uint4 tk[kTreePre ? 2 : 1], tv[kTreePre ? 8 : 1];
+  // (branch-free: rows past the tree read node n_nodes - 1 and are then
+  // zeroed, and the V part is taken by whole waves 0 and 1, so that the
+  // loads open no divergent region ahead of the DMA ring)
+  auto load_tree = [&](int key0, uint4 (&k2)[2], uint4 (&v8)[8]) {
+    const int last = max(c.n_nodes - 1, 0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int ch = tid + kMfmaThreads * r;
+      const int j = key0 + (ch >> 4);
+      const uint4 x = *reinterpret_cast<const uint4 *>(
+          k_tree + (((size_t)c.b * p.n_max + min(j, last)) * p.hkv + c.h) * kD + (ch & 15) * 8);
+      k2[r] = j < c.n_nodes ? x : zero4();
+    }
+    if (wave < 2) {  // tid < 128
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = key0 + 8 * (tid >> 4) + i;
+        const uint4 x = *reinterpret_cast<const uint4 *>(
+            v_tree + (((size_t)c.b * p.n_max + min(j, last)) * p.hkv + c.h) * kD +
+            (tid & 15) * 8);
+        v8[i] = j < c.n_nodes ? x : zero4();
+      }
+    }
+  };
+  auto load_masks = [&]() {
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
+      const int r = row_of(k);
+      const int node = r < c.rows_b ? r / c.G : 0;
+      load_mask4(tmask[k], p.tree_mask + ((size_t)c.b * p.n_max + node) * p.words, p.words);
+    }
+  };
+  if constexpr (kTreePre) {
+    if (c.n_tree > 0) {
+      load_masks();
+      load_tree(0, tk, tv);
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries and stages 0, 1
   if (ROPE) {
     // the lane holds dims 32 kk + 8 g4 + j; kk and kk + 2 are the pairs
@@ -592,20 +646,45 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   }
 
   // ---- tree tiles (split 0 only): the keys are the tree nodes themselves.
-  const __bf16 *k_tree = static_cast<const __bf16 *>(p.k_tree);
-  const __bf16 *v_tree = static_cast<const __bf16 *>(p.v_tree);
-  if (c.n_tree > 0) {
-#pragma unroll
-    for (int k = 0; k < NA; ++k) {
-      const int r = row_of(k);
-      const int node = r < c.rows_b ? r / c.G : 0;
-      load_mask4(tmask[k], p.tree_mask + ((size_t)c.b * p.n_max + node) * p.words, p.words);
-    }
-  }
+  if (!kTreePre && c.n_tree > 0) load_masks();
   for (int tt = 0; tt < c.n_tree; ++tt) {
     const int key0 = tt * kTile;
     uint8_t *sK = smem;  // stage 0 (all prefix loads have completed)
     uint8_t *sV = smem + kKBytes;
+    if constexpr (kTreePre) {
+      // K chunks as loaded; V 8 x 8 blocks transposed in registers (below)
+      if (tt > 0) load_tree(key0, tk, tv);
+      wait_vmcnt<0>();
+      lds_barrier();
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int ch = tid + kMfmaThreads * r;
+        const int R = k_row_of_key(ch >> 4);
+        *reinterpret_cast<uint4 *>(sK + R * 256 + (((ch & 15) ^ (R & 15)) << 4)) = tk[r];
+      }
+      if (tid < 128) {
+        const int dc = tid & 15, kc = tid >> 4;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int q = e >> 1;
+          uint32_t o4[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint4 &va = tv[2 * m], &vb = tv[2 * m + 1];
+            const uint32_t a = q == 0 ? va.x : q == 1 ? va.y : q == 2 ? va.z : va.w;
+            const uint32_t b2 = q == 0 ? vb.x : q == 1 ? vb.y : q == 2 ? vb.z : vb.w;
+            o4[m] = (e & 1) ? ((a >> 16) | (b2 & 0xffff0000u)) : ((a & 0xffffu) | (b2 << 16));
+          }
+          const int d = dc * 8 + e;
+          *reinterpret_cast<uint4 *>(sV + (kc >> 1) * 4096 + d * 32 +
+                                     (((kc & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4)) =
+              make_uint4(o4[0], o4[1], o4[2], o4[3]);
+        }
+      }
+      lds_barrier();
+      if (NA > 0) compute(0, key0, true);
+      continue;
+    }
     wait_vmcnt<0>();
     lds_barrier();
 #pragma unroll
