@@ -156,6 +156,10 @@ EDGE = [
     # a long prefix over one KV head: more than 32 prefix splits to combine
     ("many_splits", "llama3_8b_b1", dict(B=1, Hq=4, Hkv=1, kmax=16, stage_k_ret=[8, 4, 0],
                                          n_draft=16, prefix_list=[20000], V=2048)),
+    # over 8192 output rows merged from a few splits, a row count that is not
+    # a multiple of four, ragged prefixes (some sequences use fewer splits)
+    ("combine_rows", "qwen3_8b_b16", dict(B=5, Hq=30, Hkv=6, prefix_list=[1500, 200, 700, 64,
+                                                                         1499], V=2048)),
     # GQA group 16 with several row groups and a split prefix
     ("group16_long", "qwen3_235b_share", dict(B=2, Hq=32, Hkv=2, prefix_list=[2500, 4100],
                                               V=3000)),
