@@ -475,15 +475,20 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     bf16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
+    // all eight V operands are read before the first P V op, so that their
+    // LDS latency is paid once per half instead of once per dim block
+    bf16x8 av[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) av[d] = *reinterpret_cast<const bf16x8 *>(sV + d * 512);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < NA; ++k)
       l_acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], l_acc[k], 0, 0, 0);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sV + d * 512);
 #pragma unroll
       for (int k = 0; k < NA; ++k)
-        o[k][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[k], o[k][d], 0, 0, 0);
+        o[k][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[d], pb[k], o[k][d], 0, 0, 0);
     }
   };
   // One 64-key tile.  Up to two blocks per wave it is software-pipelined
