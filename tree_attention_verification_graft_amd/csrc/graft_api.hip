@@ -231,6 +231,7 @@ static graft_status attention_impl(graft_dtype dtype, int32_t batch, int32_t n_m
   p.rows_per_group = pl.rows_per_group;
   p.lpt = pl.mfma && pl.lpt ? 1 : 0;
   p.key_pairs = pl.mfma && pl.key_pairs ? 1 : 0;
+  p.tree_shift = pl.mfma ? pl.tree_shift : 0;
   char *ws = static_cast<char *>(workspace);
   p.part_o = pl.n_splits > 1 ? reinterpret_cast<float *>(ws) : nullptr;
   p.part_ml = pl.n_splits > 1

@@ -67,6 +67,7 @@ struct AttnParams {
   int32_t rows_per_group;  // query rows per group (multiple of 16)
   int32_t lpt;             // rank (sequence, split) pairs longest first on the device
   int32_t key_pairs;       // waves w and w + 4 share rows, one 32-key half of each tile each
+  int32_t tree_shift;      // split s covers prefix tiles [s tps - shift, (s + 1) tps - shift)
   float *part_o;           // [batch][hkv][groups][splits][rows][D]
   float *part_ml;          // [batch][hkv][groups][splits][rows][2]
 };
@@ -74,6 +75,7 @@ struct AttnPlan {
   bool mfma;
   bool lpt;  // ragged batch: launch the longest (sequence, split) work first
   bool key_pairs;  // at most 4 row blocks per group: waves pair up on the keys of each tile
+  int32_t tree_shift;  // tree tiles counted at the front of split 0 (0: none)
   int32_t n_splits, tiles_per_split, n_row_groups, rows_per_group;
   size_t part_o_bytes, part_ml_bytes;
 };

@@ -911,7 +911,9 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
     typedef const __attribute__((address_space(4))) int32_t const_i32;
     const_i32 *trow = (const_i32 *)(p.block_table + (size_t)c.b * p.max_blocks);
     const int last = p.max_blocks - 1;
-    const int pg0 = c.split * p.tiles_per_split * 4 + (c.wave & 3);
+    // split s covers prefix tiles [s * tps - shift, (s + 1) * tps - shift):
+    // the first `shift` tiles of split 0 are its tree tiles
+    const int pg0 = max(0, c.split * p.tiles_per_split - p.tree_shift) * 4 + (c.wave & 3);
     c.first_page = trow[0];
 #pragma unroll
     for (int i = 0; i < 3; ++i) c.pre_page[i] = trow[(uint32_t)min(pg0 + 4 * i, last)];
@@ -931,8 +933,8 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
 
   const int nt_prefix = (c.P + kTile - 1) / kTile;
   c.n_pages_b = (c.P + kBlock - 1) / kBlock;
-  c.t_begin = c.split * p.tiles_per_split;
-  const int t_end = min(c.t_begin + p.tiles_per_split, nt_prefix);
+  c.t_begin = max(0, c.split * p.tiles_per_split - p.tree_shift);
+  const int t_end = min((c.split + 1) * p.tiles_per_split - p.tree_shift, nt_prefix);
   c.n_pref = max(0, t_end - c.t_begin);
   c.n_tree = c.split == 0 ? (c.n_nodes + kTile - 1) / kTile : 0;
   if (c.n_pref == 0 && c.n_tree == 0) return;  // empty split
@@ -1135,7 +1137,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int P = min(max(p.prefix_len[b], 0), p.max_blocks * kBlock);
   const int nt_prefix = (P + kTile - 1) / kTile;
   const int active =
-      min(p.n_splits, max(1, (nt_prefix + p.tiles_per_split - 1) / p.tiles_per_split));
+      min(p.n_splits,
+          max(1, (nt_prefix + p.tree_shift + p.tiles_per_split - 1) / p.tiles_per_split));
   const size_t base = (((size_t)b * p.hkv + h) * p.n_row_groups + rg) * p.n_splits;
   const size_t stride = (size_t)p.rows_per_group;  // partial rows between splits
   const float *ml = p.part_ml + (base * stride + rl) * 2;
@@ -1326,6 +1329,18 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
           pl.n_splits = splits;
           pl.key_pairs = pairs;
         }
+      }
+    }
+    // Split 0 also runs the tree tiles, so with equal prefix shares it ends
+    // last.  Uniform batches count the tree tiles as the first tiles of
+    // split 0 instead, when that keeps the split count and leaves split 0 at
+    // least one prefix tile (so that the splits with prefix work stay the
+    // first ones, as the combine assumes).
+    if (!ragged && pl.n_splits > 1) {
+      const int tps = (tiles + tree_tiles + pl.n_splits - 1) / pl.n_splits;
+      if (tps >= tree_tiles + 1 && (tiles + tree_tiles + tps - 1) / tps == pl.n_splits) {
+        pl.tiles_per_split = tps;
+        pl.tree_shift = tree_tiles;
       }
     }
   } else {
