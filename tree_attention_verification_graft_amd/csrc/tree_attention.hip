@@ -865,7 +865,8 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
         const int b = t / S, sp = t % S;
         const int P = min(max(p.prefix_len[b], 0), p.max_blocks * kBlock);
         const int tiles = (P + kTile - 1) / kTile;
-        w = max(0, min(p.tiles_per_split, tiles - sp * p.tiles_per_split));
+        const int tb = max(0, sp * p.tiles_per_split - p.tree_shift);
+        w = max(0, min((sp + 1) * p.tiles_per_split - p.tree_shift, tiles) - tb);
         if (sp == 0) w += (min(max(p.n_nodes[b], 0), p.n_max) + kTile - 1) / kTile;
         s_w[t] = w;
       }
@@ -1332,11 +1333,11 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
       }
     }
     // Split 0 also runs the tree tiles, so with equal prefix shares it ends
-    // last.  Uniform batches count the tree tiles as the first tiles of
-    // split 0 instead, when that keeps the split count and leaves split 0 at
-    // least one prefix tile (so that the splits with prefix work stay the
-    // first ones, as the combine assumes).
-    if (!ragged && pl.n_splits > 1) {
+    // last.  The tree tiles count as the first tiles of split 0 instead,
+    // when that keeps the split count and leaves split 0 at least one prefix
+    // tile (so that the splits with prefix work stay the first ones, as the
+    // combine assumes).
+    if (pl.n_splits > 1) {
       const int tps = (tiles + tree_tiles + pl.n_splits - 1) / pl.n_splits;
       if (tps >= tree_tiles + 1 && (tiles + tree_tiles + tps - 1) / tps == pl.n_splits) {
         pl.tiles_per_split = tps;
