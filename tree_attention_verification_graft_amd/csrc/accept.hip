@@ -57,6 +57,29 @@ __device__ inline unsigned long long pack(uint32_t ord, int idx) {
 __device__ inline unsigned long long umax64(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
+// Order-preserving int16 keys of the two bf16 values in a word, by packed
+// 16-bit integer ops: a negative value flips its magnitude bits (so larger
+// magnitudes order lower) and moves up by one, which folds -0 onto +0.  A
+// key of -32768 is below every value's (the most negative finite value maps
+// to -32639), so it marks entries outside the chunk.
+typedef short short2v __attribute__((ext_vector_type(2)));
+__device__ inline short2v okey2(uint32_t w) {
+  const short2v x = __builtin_bit_cast(short2v, w);
+  const short2v s = x >> (short2v){15, 15};  // 0 or -1 per half
+  return (x ^ (s & (short2v){0x7fff, 0x7fff})) - s;
+}
+// The bf16 bits of a key (either zero for key 0).
+__device__ inline uint32_t key_bf16(int key) {
+  return key >= 0 ? (uint32_t)key : (uint32_t)(((key - 1) ^ 0x7fff) & 0xffff);
+}
+__device__ inline int wave_max_i32(int v) {
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ inline int wave_min_i32(int v) {
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
+  return v;
+}
 __device__ inline unsigned long long wave_max64(unsigned long long v) {
   for (int off = 32; off > 0; off >>= 1) v = umax64(v, __shfl_xor(v, off));
   return v;
@@ -90,20 +113,60 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks_kernel(AcceptParams p)
         v[k] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
+    if (BF16) {
+      // The chunk's largest key by packed 16-bit maxima (two values per
+      // op), then the lowest index holding it, searched only by the threads
+      // whose own maximum it is.
+      short2v acc = (short2v){-32768, -32768};
+#pragma unroll
+      for (int k = 0; k < kLoads; ++k) {
+        const int e = lo + (k * kThreads + threadIdx.x) * kPer;
+        if (e >= hi) continue;
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_elementwise_max(acc, okey2(w[q]));
+      }
+      const int tmax = max((int)acc.x, (int)acc.y);
+      __shared__ int s_red[kThreads / 64];
+      int m = wave_max_i32(tmax);
+      if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+      __syncthreads();
+      m = s_red[0];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) m = max(m, s_red[w]);
+      int idx = 0x7fffffff;
+      if (tmax == m) {
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+          const int e = lo + (k * kThreads + threadIdx.x) * kPer;
+          if (e >= hi) continue;
+          const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const short2v kq = okey2(w[q]);
+            if (kq.x == m) idx = min(idx, e + 2 * q);
+            if (kq.y == m) idx = min(idx, e + 2 * q + 1);
+          }
+        }
+      }
+      idx = wave_min_i32(idx);
+      __syncthreads();  // every wave has read s_red
+      if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = idx;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int i_min = s_red[0];
+        for (int w = 1; w < kThreads / 64; ++w) i_min = min(i_min, s_red[w]);
+        p.partial[(size_t)row * p.chunks + c] = pack(ord_bf16(key_bf16(m)), i_min);
+      }
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int e = lo + (k * kThreads + threadIdx.x) * kPer;
       if (e >= hi) continue;
       const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (BF16) {
-          best = umax64(best, pack(ord_bf16(w[q] & 0xffffu), e + 2 * q));
-          best = umax64(best, pack(ord_bf16(w[q] >> 16), e + 2 * q + 1));
-        } else {
-          best = umax64(best, pack(ord_f32(w[q]), e + q));
-        }
-      }
+      for (int q = 0; q < 4; ++q) best = umax64(best, pack(ord_f32(w[q]), e + q));
     }
   } else {
     constexpr int kScalar = kChunk / kThreads;  // scalar loads per thread
