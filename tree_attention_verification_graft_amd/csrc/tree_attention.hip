@@ -116,6 +116,14 @@ __device__ inline float group4_sum(float x) {
 // accumulator and the row sum share the offset), which saves most rescales.
 constexpr float kRescaleLog2 = 8.f;
 
+// Prefix splits holding work for a sequence of nt_prefix prefix tiles (split
+// 0 always, for its tree tiles).  A sequence with one has its output written
+// by the attention kernel itself, and the combine skips its rows.
+__device__ inline int active_splits(const AttnParams &p, int nt_prefix) {
+  return min(p.n_splits,
+             max(1, (nt_prefix + p.tree_shift + p.tiles_per_split - 1) / p.tiles_per_split));
+}
+
 // LDS row of the K tile that holds key `k` (0..63) of the tile.  Rows are in
 // the order the transposed score blocks use: score block kb = 2*kp + half,
 // row 4*g + i holds key 32*kp + 8*g + 4*half + i.
@@ -219,6 +227,7 @@ struct MfmaCtx {
   // key pairs, waves w and w + 4 own the same blocks (wslot = w & 3,
   // wstride 4) and each takes one 32-key half (khalf) of every tile.
   int wslot, wstride, khalf;
+  bool direct;  // this sequence has one active split: write the output itself
   uint32_t lds0;  // LDS byte address of stage 0
   // The wave's page-table entries for the split's first three tiles and the
   // sequence's first page, loaded before the prefix length is known (indices
@@ -804,7 +813,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     const int r = row_of(k);
     if (r >= c.rows_b) continue;
     const int rl = r - c.row0;
-    if (p.n_splits == 1) {
+    if (c.direct) {
       const float inv = 1.f / l;
       const int node = r / c.G;
       const int hq = c.h * c.G + r % c.G;
@@ -938,6 +947,7 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   const int t_end = min((c.split + 1) * p.tiles_per_split - p.tree_shift, nt_prefix);
   c.n_pref = max(0, t_end - c.t_begin);
   c.n_tree = c.split == 0 ? (c.n_nodes + kTile - 1) / kTile : 0;
+  c.direct = active_splits(p, nt_prefix) == 1;
   if (c.n_pref == 0 && c.n_tree == 0) return;  // empty split
 
 
@@ -1089,7 +1099,7 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnParams p) {
   for (int t = 0; t < n_tree; ++t) chunk(t * 64, true);
 
   if (!row_ok) return;
-  if (p.n_splits == 1) {
+  if (active_splits(p, nt_prefix) == 1) {
     const float inv = 1.f / l_run;
     T *out = static_cast<T *>(p.out) + (((size_t)b * p.n_max + node) * p.hq + hq) * D;
 #pragma unroll
@@ -1137,9 +1147,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int rl = r % p.rows_per_group;
   const int P = min(max(p.prefix_len[b], 0), p.max_blocks * kBlock);
   const int nt_prefix = (P + kTile - 1) / kTile;
-  const int active =
-      min(p.n_splits,
-          max(1, (nt_prefix + p.tree_shift + p.tiles_per_split - 1) / p.tiles_per_split));
+  const int active = active_splits(p, nt_prefix);
+  if (active == 1) return;  // written by the attention kernel
   const size_t base = (((size_t)b * p.hkv + h) * p.n_row_groups + rg) * p.n_splits;
   const size_t stride = (size_t)p.rows_per_group;  // partial rows between splits
   const float *ml = p.part_ml + (base * stride + rl) * 2;
