@@ -9,15 +9,16 @@
 // SIMD) owns a (sequence, KV head, row group, prefix split).  The query rows of a KV head
 // are its tree nodes times the query heads of the group.  K and V tiles of 64
 // keys are staged from the paged cache into LDS once and shared by all waves;
-// each wave owns up to NB blocks of 16 query rows.  Scores are computed
+// each wave owns up to NB blocks of 16 query rows (with at most 4 blocks per
+// group, waves w and w + 4 share blocks and split each tile's keys).  Scores are computed
 // transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: each lane then holds
 // one query column and 16 keys of the tile, so the softmax reductions are
 // in-lane plus two cross-lane steps, and the score accumulators convert
 // directly into the P^T operand of O^T = V^T P^T without any shuffle (keys are
 // placed in LDS in the order that makes this so).  V pages are dim-major in
 // the cache, so V^T tiles are contiguous copies.  Prefix splits write fp32
-// partial (O, max, sum) and a combine kernel merges them; a single split
-// writes the output directly.
+// partial (O, max, sum) and a combine kernel merges them; a sequence with a
+// single active split writes its output directly.
 //
 // Wavefront path (fp32, or fewer than 16 query rows): one wave per query
 // row, keys spread over lanes for q.k, head dims over lanes for P V.
