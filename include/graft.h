@@ -179,6 +179,34 @@ size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch,
                                            int32_t n_max, int32_t hq, int32_t hkv,
                                            int32_t head_dim, int32_t max_prefix,
                                            int64_t sum_prefix);
+/*
+ * graft_tree_attention_plan -- the launch plan graft_tree_attention (and
+ * graft_tree_attention_rope) uses for these shapes: which kernel runs and how
+ * its work is cut.  Host-only, enqueues nothing; the arguments mean what they
+ * mean for graft_tree_attention.  Returns GRAFT_ERR_INVALID_ARG for a null
+ * `plan` and the call's own shape errors otherwise.
+ *   matrix_cores     1: the matrix-core kernel (bf16, head_dim 128, at least
+ *                    16 query rows per KV head); 0: one wave per query row
+ *   n_row_groups     workgroups along the query rows of one KV head
+ *   rows_per_group   query rows (node x group + head-in-group) per row group
+ *   n_splits         prefix splits; above 1 a combine launch merges them
+ *   tiles_per_split  64-key prefix tiles per split
+ *   tree_shift       split s covers prefix tiles [s tps - shift, (s+1) tps -
+ *                    shift): the tree's own tiles count as split 0's first
+ *   key_pairs        1: two waves share each 16-row block, one half of each
+ *                    64-key tile each
+ *   longest_first    1: ragged batch, (sequence, split) work started longest
+ *                    first
+ *   workgroups       workgroups of the attention launch
+ */
+typedef struct {
+  int32_t matrix_cores, n_row_groups, rows_per_group, n_splits, tiles_per_split,
+      tree_shift, key_pairs, longest_first, workgroups;
+} graft_attention_plan;
+graft_status graft_tree_attention_plan(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                       int32_t hq, int32_t hkv, int32_t head_dim,
+                                       int32_t max_prefix, int64_t sum_prefix,
+                                       graft_attention_plan *plan);
 graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_max,
                                   int32_t hq, int32_t hkv, int32_t head_dim,
                                   const void *q, const void *k_tree,

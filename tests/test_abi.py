@@ -212,3 +212,35 @@ def test_rope_variants_validation():
     assert app(rope=None) == -1
     assert app(dt=9) == -1
     assert app(b=0) == 0
+
+
+def test_attention_plan_query():
+    """The plan query is host-only and describes the launch of each
+    workload's shapes: the matrix-core kernel for bf16 with head_dim 128 and
+    16 or more rows, the wavefront kernel otherwise; the plan tiles every
+    prefix tile exactly once; a null plan is rejected."""
+    bf = G.GRAFT_BF16
+    shapes = {  # (dtype, batch, n_max, hq, hkv, D, max_prefix, sum_prefix)
+        "llama3_8b_b1": (bf, 1, 61, 32, 8, 128, 2048, 2048),
+        "qwen3_8b_b16": (bf, 16, 65, 32, 8, 128, 4096, 36000),
+        "llama31_8b_64k": (bf, 1, 65, 32, 8, 128, 65536, 65536),
+        "qwen3_235b_share": (bf, 32, 65, 64, 4, 128, 8192, 32 * 8192),
+        "bf16_head_dim_64": (bf, 2, 17, 8, 2, 64, 300, 600),
+        "tiny_f32": (G.GRAFT_F32, 1, 17, 4, 1, 64, 128, 128),
+    }
+    for name, (dt, B, n_max, hq, hkv, D, mp, sp) in shapes.items():
+        pl = G.graft_tree_attention_plan(dt, B, n_max, hq, hkv, D, mp, sp)
+        rows = n_max * (hq // hkv)
+        assert pl["matrix_cores"] == int(dt == bf and D == 128 and rows >= 16), name
+        assert pl["n_row_groups"] * pl["rows_per_group"] >= rows, name
+        tiles = -(-mp // 64)
+        tps, shift = pl["tiles_per_split"], pl["tree_shift"]
+        # split s covers prefix tiles [s tps - shift, (s + 1) tps - shift)
+        covered = [t for s in range(pl["n_splits"])
+                   for t in range(max(0, s * tps - shift), min(tiles, (s + 1) * tps - shift))]
+        assert covered == list(range(tiles)), name
+        assert pl["workgroups"] >= B * hkv * pl["n_splits"] * pl["n_row_groups"], name
+    assert lib.graft_tree_attention_plan(bf, 1, 17, 8, 2, 128, 100, 0, None) == -1
+    assert lib.graft_tree_attention_plan(bf, 1, 17, 8, 3, 128, 100, 0,
+                                         ctypes.byref(G.AttentionPlan())) == -1
+

@@ -60,8 +60,12 @@ def check_attention(w, out_gpu, tree, rows=None):
     excess = max(float((np.abs(got[b, i, h] - ref[b, i, h])
                         - OUT_ROUND[w.dtype] * np.abs(ref[b, i, h])).max())
                  for (b, i, h) in rows)
-    assert np.isfinite(err) and excess <= TOL[w.dtype], (
-        f"attention max-abs {err} (beyond output rounding: {excess})")
+    _say(f"[parity] attention on {len(rows)} rows: max-abs {err:.3e}, "
+         f"beyond output rounding {excess:.3e} (bar {TOL[w.dtype]})")
+    # the bar on the plain max-abs error, and the same bar on what is left
+    # after the output's own rounding to its storage type
+    assert np.isfinite(err) and err <= TOL[w.dtype], f"attention max-abs {err}"
+    assert excess <= TOL[w.dtype], f"attention error beyond output rounding {excess}"
     return err
 
 
@@ -145,6 +149,10 @@ EDGE = [
     # no drafts at all (pure retrieval) and single-draft sequences
     ("no_drafts", "llama3_8b_b1", dict(B=3, Hq=8, Hkv=2, prefix_list=[100, 200, 5],
                                        n_draft_list=[0, 1, 60], V=1024)),
+    # bf16 with head_dim 64 takes the wavefront path at any row count (244
+    # query rows per KV head here)
+    ("bf16_head_dim_64", "llama3_8b_b1", dict(B=2, Hq=8, Hkv=2, D=64, prefix_list=[300, 1000],
+                                              V=2048)),
     # fewer than 16 query rows: bf16 takes the wavefront path
     ("few_rows_bf16", "llama3_8b_b1", dict(B=2, Hq=8, Hkv=2, kmax=2, stage_k_ret=[1, 1, 0],
                                           n_draft=4, prefix_list=[129, 300], V=512)),
@@ -225,15 +233,49 @@ def test_attention_is_deterministic():
 # attention checked on sampled rows
 # ----------------------------------------------------------------------------
 
-def _sample_rows(w, tree, n, seed):
+def plan_rows(w, tree, n_full_seqs, seed):
+    """Attention rows for a full-size check, chosen against the launch plan
+    the call uses: every row of one KV head (h = b mod Hkv) for n_full_seqs
+    sequences spread over the batch, one random row in every (sequence, KV
+    head, row group) workgroup set of the plan (each such row's output merges
+    every prefix split of its group), and the deepest node of every
+    sequence.  Returns the rows and the plan, after asserting the coverage."""
+    from tree_attention_verification_graft_amd import binding as G
+    dt = G.GRAFT_BF16 if w.dtype == "bf16" else G.GRAFT_F32
+    plan = G.graft_tree_attention_plan(dt, w.B, w.n_max, w.Hq, w.Hkv, w.D, w.max_prefix,
+                                       int(w.prefix_len.sum()))
+    _say(f"[parity] {w.name} plan: {plan}")
+    Gq = w.Hq // w.Hkv
+    rpg = plan["rows_per_group"]
     rng = np.random.default_rng(seed)
+    nn = [int(x) for x in tree["n_nodes"]]
     rows = set()
-    for b in range(w.B):  # the last node of every sequence (deepest tree keys)
-        rows.add((b, int(tree["n_nodes"][b]) - 1, int(rng.integers(w.Hq))))
-    while len(rows) < n:
-        b = int(rng.integers(w.B))
-        rows.add((b, int(rng.integers(int(tree["n_nodes"][b]))), int(rng.integers(w.Hq))))
-    return sorted(rows)
+    full = sorted({round(k * (w.B - 1) / max(1, n_full_seqs - 1)) for k in range(n_full_seqs)})
+    for b in full:
+        h = b % w.Hkv
+        rows.update((b, i, h * Gq + g) for i in range(nn[b]) for g in range(Gq))
+    groups = set()
+    for b in range(w.B):
+        rows.add((b, nn[b] - 1, int(rng.integers(w.Hq))))
+        for h in range(w.Hkv):
+            for rg in range(plan["n_row_groups"]):
+                lo, hi = rg * rpg, min((rg + 1) * rpg, nn[b] * Gq)
+                if lo >= hi:
+                    continue  # no rows of this sequence in the group
+                groups.add((b, h, rg))
+                r = int(rng.integers(lo, hi))
+                rows.add((b, r // Gq, h * Gq + r % Gq))
+    covered = {(b, h // Gq, (i * Gq + h % Gq) // rpg) for (b, i, h) in rows}
+    assert groups <= covered, "a workgroup set of the plan has no checked row"
+    _say(f"[parity] {w.name}: {len(rows)} rows cover all {len(groups)} (sequence, KV head, "
+         f"row group) sets x {plan['n_splits']} splits; every row of one KV head of "
+         f"sequences {full}")
+    return sorted(rows), plan
+
+
+# sequences whose rows of one KV head are all checked at full size
+FULL_SEQS = {"tiny_f32": 1, "llama3_8b_b1": 1, "qwen3_8b_b16": 16, "llama31_8b_64k": 1,
+             "qwen3_235b_share": 4}
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -244,8 +286,30 @@ def test_full_size(name):
     if seed:
         m_ids = O.update_adjacency(w.m_ids, w.m_scores, w.prompt[None],
                                    np.array([len(w.prompt) - 2]))[0]
-    rows = _sample_rows(w, oracle_tree(w, m_ids), 48, 7)
+    rows, _ = plan_rows(w, oracle_tree(w, m_ids), FULL_SEQS[name], 7)
     run_full_check(w, attn_rows=rows, seed_prompt=seed)
+
+
+# The Llama-3-8B workload lists its retrieval budgets for d0/d1/d5 as
+# 0/16/32; read literally (d0 -> 0) that contradicts the rule that an earlier
+# stage gets more retrieval, so the workloads take (32, 16, 0).  The literal
+# order runs here through the same calls: at oracle size with every stage
+# outcome forced in turn, and at full size.
+LITERAL_K_RET = [0, 16, 32]
+
+
+def test_literal_k_ret_order_small():
+    w = W.make("llama3_8b_b1", B=8, Hq=8, Hkv=2, prefix=(100, 900), V=4096, conf="forced",
+               stage_k_ret=LITERAL_K_RET)
+    ref = oracle_tree(w)
+    assert sorted(set(ref["stage"].tolist())) == [-1, 0, 1, 2]
+    run_full_check(w)
+
+
+def test_literal_k_ret_order_full_size():
+    w = W.make("llama3_8b_b1", stage_k_ret=LITERAL_K_RET)
+    rows, _ = plan_rows(w, oracle_tree(w), 1, 11)
+    run_full_check(w, attn_rows=rows)
 
 
 UPDATE_TREE = [(n, SMALL[n]) for n in W.CONFIG_ORDER] + [

@@ -24,6 +24,11 @@ SRC = inspect.getsource(real)
 
 MUTANTS = [
     ("gate not strict", "if c_d < np.float32(tau):", "if c_d <= np.float32(tau):"),
+    ("c_d mean for max", "c_d = max(at_d)", "c_d = np.float32(sum(at_d) / len(at_d))"),
+    ("c_d min for max", "c_d = max(at_d)", "c_d = min(at_d)"),
+    ("c_d sum for max", "c_d = max(at_d)", "c_d = np.float32(sum(at_d))"),
+    ("c_d from the first node", "c_d = max(at_d)", "c_d = at_d[0]"),
+    ("K_ret order reversed", "k_ret = stage_k_ret[stage]", "k_ret = stage_k_ret[len(stage_k_ret) - 1 - stage]"),
     ("firing level dropped", "if depth[i] <= stage_depth[stage]]", "if depth[i] < stage_depth[stage]]"),
     ("cap keeps worst drafts", "key=lambda i: (-float(path_min[i]), i)", "key=lambda i: (float(path_min[i]), i)"),
     ("cap by own conf", "path_min.append(c if parent[i] < 0 else min(c, path_min[parent[i]]))", "path_min.append(c)"),
@@ -43,6 +48,7 @@ MUTANTS = [
     ("argmax last index", "am[b, i] = int(np.argmax(row))", "am[b, i] = int(len(row) - 1 - np.argmax(row[::-1]))"),
     ("update ties by id desc", "key=lambda kv: (-kv[1], kv[0]))[:S]", "key=lambda kv: (-kv[1], -kv[0]))[:S]"),
     ("update forgets old score", "cand[v] = cand.get(v, 0.0) + float(c)", "cand[v] = float(c)"),
+    ("update ignores repeated transitions", "counts = Counter(transitions(path_tokens, accept_len))", "counts = Counter(set(transitions(path_tokens, accept_len)))"),
     ("bonus transition dropped", "for k in range(L + 1):", "for k in range(L):"),
     ("commit one slot late", "            t = P + j\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree", "            t = P + j + 1\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree"),
     ("commit drops the deepest node", "        for j in range(L + 1):\n            node = int(path_nodes[b][j])\n            t = P + j\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree", "        for j in range(L):\n            node = int(path_nodes[b][j])\n            t = P + j\n            page = int(block_table[b][t // blk])\n            k[page, :, t % blk, :] = k_tree"),
@@ -73,13 +79,15 @@ def _mutant_module(old, new):
 def _pin_calls():
     """Every pin test with its parameter values, as zero-arg callables."""
     calls = []
-    for idx in range(4):
+    for idx in range(6):
         calls.append(lambda idx=idx: T_bt.test_golden_examples(idx))
     for s in range(40):
         calls.append(lambda s=s: T_bt.test_invariants_random(s))
     for s in range(30):
         calls.append(lambda s=s: T_bt.test_kept_set_is_best_by_path_confidence(s))
     calls += [T_bt.test_stage_gate_readings, T_bt.test_no_retrieval_mode_is_topk_drafts]
+    for order in sorted(T_bt.K_RET_ORDERS):
+        calls.append(lambda order=order: T_bt.test_k_ret_orders_on_the_llama3_8b_shape(order))
     for P in [0, 1, 16, 37]:
         calls.append(lambda P=P: T_at.test_chain_equals_causal_attention(P))
     for s in range(12):

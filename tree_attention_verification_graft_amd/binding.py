@@ -24,7 +24,8 @@ MAX_TOP_S = 32
 
 EXPORTED = [
     "graft_build_tree", "graft_tree_attention_workspace_size",
-    "graft_tree_attention", "graft_accept_workspace_size", "graft_accept",
+    "graft_tree_attention_plan", "graft_tree_attention", "graft_accept_workspace_size",
+    "graft_accept",
     "graft_accept_sample_workspace_size", "graft_accept_sample",
     "graft_update_adjacency_workspace_size", "graft_update_adjacency",
     "graft_update_adjacency_tree_workspace_size", "graft_update_adjacency_tree",
@@ -35,6 +36,12 @@ EXPORTED = [
 
 class GraftError(RuntimeError):
     pass
+
+
+class AttentionPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "matrix_cores", "n_row_groups", "rows_per_group", "n_splits", "tiles_per_split",
+        "tree_shift", "key_pairs", "longest_first", "workgroups")]
 
 
 class TreeConfig(ctypes.Structure):
@@ -84,6 +91,7 @@ def _load(path=LIB_PATH):
         "graft_build_tree": [ctypes.POINTER(TreeConfig), I, I, P, P, P, P, P, P, P, I, I,
                              P, P, P, P, P, P, P],
         "graft_tree_attention_workspace_size": [I, I, I, I, I, I, I, I64],
+        "graft_tree_attention_plan": [I, I, I, I, I, I, I, I64, ctypes.POINTER(AttentionPlan)],
         "graft_tree_attention": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, I64, P, P,
                                  ctypes.c_float, P, P, SZ, P],
         "graft_accept_workspace_size": [I, I, I],
@@ -194,6 +202,17 @@ def graft_tree_attention_workspace_size(dtype_code, batch, n_max, hq, hkv, head_
                                         max_prefix, sum_prefix=0):
     return int(_lib.graft_tree_attention_workspace_size(dtype_code, batch, n_max, hq, hkv,
                                                         head_dim, max_prefix, int(sum_prefix)))
+
+
+def graft_tree_attention_plan(dtype_code, batch, n_max, hq, hkv, head_dim, max_prefix,
+                              sum_prefix=0) -> dict:
+    """The attention launch plan for these shapes, as a dict of the
+    graft_attention_plan fields."""
+    pl = AttentionPlan()
+    _check(_lib.graft_tree_attention_plan(dtype_code, batch, n_max, hq, hkv, head_dim,
+                                          int(max_prefix), int(sum_prefix), ctypes.byref(pl)),
+           "graft_tree_attention_plan")
+    return {n: int(getattr(pl, n)) for n, _ in AttentionPlan._fields_}
 
 
 def graft_tree_attention(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,

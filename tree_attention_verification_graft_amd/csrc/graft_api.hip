@@ -168,6 +168,28 @@ size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch, int
   return align_up(pl.part_o_bytes, 256) + align_up(pl.part_ml_bytes, 256);
 }
 
+graft_status graft_tree_attention_plan(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                       int32_t hq, int32_t hkv, int32_t head_dim,
+                                       int32_t max_prefix, int64_t sum_prefix,
+                                       graft_attention_plan *plan) {
+  g_error[0] = 0;
+  REQUIRE(plan, GRAFT_ERR_INVALID_ARG, "graft_tree_attention_plan: plan is null");
+  const graft_status st = check_attn_shape(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
+  if (st != GRAFT_OK) return st;
+  const AttnPlan pl =
+      plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix, sum_prefix);
+  plan->matrix_cores = pl.mfma ? 1 : 0;
+  plan->n_row_groups = pl.n_row_groups;
+  plan->rows_per_group = pl.rows_per_group;
+  plan->n_splits = pl.n_splits;
+  plan->tiles_per_split = pl.tiles_per_split;
+  plan->tree_shift = pl.mfma ? pl.tree_shift : 0;
+  plan->key_pairs = pl.mfma && pl.key_pairs ? 1 : 0;
+  plan->longest_first = pl.mfma && pl.lpt ? 1 : 0;
+  plan->workgroups = (int32_t)attention_workgroups(pl, batch, hkv);
+  return GRAFT_OK;
+}
+
 static graft_status attention_impl(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hq,
                                    int32_t hkv, int32_t head_dim, const void *q,
                                    const void *k_tree, const void *v_tree, const void *k_cache,

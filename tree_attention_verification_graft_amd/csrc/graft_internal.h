@@ -83,6 +83,8 @@ struct AttnPlan {
 // sequence is taken at max_prefix); it only steers the plan.
 AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t hq,
                         int32_t hkv, int32_t head_dim, int32_t max_prefix, int64_t sum_prefix);
+// Workgroups of the attention launch of a plan.
+long attention_workgroups(const AttnPlan &pl, int32_t batch, int32_t hkv);
 void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream);
 void launch_attention_wave(graft_dtype dtype, const AttnParams &p, hipStream_t stream);
 void launch_attention_combine(graft_dtype dtype, const AttnParams &p,

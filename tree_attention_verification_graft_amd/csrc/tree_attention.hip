@@ -1382,6 +1382,14 @@ void launch_mfma(const AttnParams &p, dim3 grid, hipStream_t stream) {
 }
 }  // namespace
 
+long attention_workgroups(const AttnPlan &pl, int32_t batch, int32_t hkv) {
+  if (pl.mfma) {
+    const long clusters = (long)batch * hkv * pl.n_splits;
+    return 8L * pl.n_row_groups * ((clusters + 7) / 8);
+  }
+  return (long)pl.n_splits * hkv * (pl.rows_per_group / 4) * batch;
+}
+
 void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream) {
   const long clusters = (long)p.batch * p.hkv * p.n_splits;
   dim3 grid((unsigned)(8 * p.n_row_groups * ((clusters + 7) / 8)));

@@ -58,12 +58,12 @@ class DeviceStep:
         self.v_cache = to_device(w.v_cache, d)
         self.logits = to_device(w.logits if logits is None else logits, d)
         # outputs
-        self.tree_token = torch.empty((B, self.n_max), dtype=i32, device=d)
+        self.tree_token = torch.zeros((B, self.n_max), dtype=i32, device=d)
         self.tree_parent = torch.empty_like(self.tree_token)
         self.tree_pos = torch.empty_like(self.tree_token)
-        self.tree_mask = torch.empty((B, self.n_max, self.words), dtype=i32, device=d)
-        self.n_nodes = torch.empty((B,), dtype=i32, device=d)
-        self.stage = torch.empty((B,), dtype=i32, device=d)
+        self.tree_mask = torch.zeros((B, self.n_max, self.words), dtype=i32, device=d)
+        self.n_nodes = torch.zeros((B,), dtype=i32, device=d)
+        self.stage = torch.zeros((B,), dtype=i32, device=d)
         self.out = torch.empty_like(self.q)
         self.argmax = torch.empty((B, self.n_max), dtype=i32, device=d)
         self.accept_len = torch.empty((B,), dtype=i32, device=d)
