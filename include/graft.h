@@ -221,6 +221,34 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
                                   hipStream_t stream);
 
 /*
+ * graft_tree_attention_noalloc -- graft_tree_attention without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, layouts, results and launch plan as graft_tree_attention;
+ * the split partials go to a scratch array that the library holds in device
+ * memory, GRAFT_NOALLOC_SCRATCH_BYTES on each GPU it runs on, from the
+ * first call on that GPU until the process ends.  The call allocates and
+ * frees nothing (the first call on a device looks up that device's copy of
+ * the array).  A plan whose partials need more than the array holds is
+ * rejected with GRAFT_ERR_WORKSPACE before any launch
+ * (graft_tree_attention_workspace_size gives the need).  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (concurrent
+ * streams, or threads) race and must be ordered by the caller.
+ */
+#define GRAFT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+graft_status graft_tree_attention_noalloc(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                          int32_t hq, int32_t hkv, int32_t head_dim,
+                                          const void *q, const void *k_tree,
+                                          const void *v_tree, const void *k_cache,
+                                          const void *v_cache, int32_t block_size,
+                                          const int32_t *block_table,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t *prefix_len, int32_t max_prefix,
+                                          int64_t sum_prefix, const uint32_t *tree_mask,
+                                          const int32_t *n_nodes, float scale, void *out,
+                                          hipStream_t stream);
+
+/*
  * graft_tree_attention_rope -- graft_tree_attention for unrotated queries
  * and tree keys: the rotary position embedding at each node's tree position
  * is fused into their loads (architecture paragraph: the tree-attention

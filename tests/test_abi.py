@@ -244,3 +244,19 @@ def test_attention_plan_query():
     assert lib.graft_tree_attention_plan(bf, 1, 17, 8, 3, 128, 100, 0,
                                          ctypes.byref(G.AttentionPlan())) == -1
 
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """A plan whose split partials exceed the library's scratch is rejected
+    before anything touches the device; the limit is the header's."""
+    text = open(HEADER).read()
+    assert "#define GRAFT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    bf = G.GRAFT_BF16
+    # 8 sequences of 64k tokens with the Qwen3-235B head share (64 / 4):
+    # prefix splits of 65 x 16 query rows per KV head
+    shape = (bf, 8, 65, 64, 4, 128, 65536, 8 * 65536)
+    need = lib.graft_tree_attention_workspace_size(*shape)
+    assert need > (64 << 20)
+    args = [bf, 8, 65, 64, 4, 128] + [FAKE] * 5 + [16, FAKE, 4100, FAKE, 65536, 8 * 65536,
+                                                  FAKE, FAKE, ctypes.c_float(0.1), FAKE, None]
+    assert lib.graft_tree_attention_noalloc(*args) == -3
+    assert b"scratch" in lib.graft_last_error()

@@ -24,8 +24,8 @@ MAX_TOP_S = 32
 
 EXPORTED = [
     "graft_build_tree", "graft_tree_attention_workspace_size",
-    "graft_tree_attention_plan", "graft_tree_attention", "graft_accept_workspace_size",
-    "graft_accept",
+    "graft_tree_attention_plan", "graft_tree_attention", "graft_tree_attention_noalloc",
+    "graft_accept_workspace_size", "graft_accept",
     "graft_accept_sample_workspace_size", "graft_accept_sample",
     "graft_update_adjacency_workspace_size", "graft_update_adjacency",
     "graft_update_adjacency_tree_workspace_size", "graft_update_adjacency_tree",
@@ -94,6 +94,8 @@ def _load(path=LIB_PATH):
         "graft_tree_attention_plan": [I, I, I, I, I, I, I, I64, ctypes.POINTER(AttentionPlan)],
         "graft_tree_attention": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, I64, P, P,
                                  ctypes.c_float, P, P, SZ, P],
+        "graft_tree_attention_noalloc": [I, I, I, I, I, I, P, P, P, P, P, I, P, I, P, I, I64, P,
+                                         P, ctypes.c_float, P, P],
         "graft_accept_workspace_size": [I, I, I],
         "graft_accept": [I, I, I, I, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "graft_accept_sample_workspace_size": [I, I, I, I],
@@ -239,6 +241,32 @@ def graft_tree_attention(q, k_tree, v_tree, k_cache, v_cache, block_table, prefi
                                    float(scale), _ptr(out), _ptr(workspace), ws_bytes,
                                    _stream(stream))
     _check(st, "graft_tree_attention")
+
+
+def graft_tree_attention_noalloc(q, k_tree, v_tree, k_cache, v_cache, block_table,
+                                 prefix_len, max_prefix, tree_mask, n_nodes, scale, out,
+                                 stream=None, sum_prefix=0):
+    """graft_tree_attention with the library's own device scratch in place of
+    a caller workspace."""
+    B, n_max, hq, D = q.shape
+    hkv = k_tree.shape[2]
+    nblk, _, blk, _ = k_cache.shape
+    dt = _dtype_code(q)
+    for t, n in ((k_tree, "k_tree"), (v_tree, "v_tree")):
+        _expect(t, q.dtype, (B, n_max, hkv, D), n)
+    _expect(k_cache, q.dtype, (nblk, hkv, blk, D), "k_cache")
+    _expect(v_cache, q.dtype, (nblk, hkv, D, blk), "v_cache")
+    _expect(out, q.dtype, (B, n_max, hq, D), "out")
+    _expect(tree_mask, torch.int32, (B, n_max, mask_words(n_max)), "tree_mask")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise GraftError("block_table: expected int32 [batch][max_blocks]")
+    st = _lib.graft_tree_attention_noalloc(dt, B, n_max, hq, hkv, D, _ptr(q), _ptr(k_tree),
+                                           _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), blk,
+                                           _ptr(block_table), block_table.shape[1],
+                                           _ptr(prefix_len), int(max_prefix), int(sum_prefix),
+                                           _ptr(tree_mask), _ptr(n_nodes), float(scale),
+                                           _ptr(out), _stream(stream))
+    _check(st, "graft_tree_attention_noalloc")
 
 
 def graft_tree_attention_rope(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,

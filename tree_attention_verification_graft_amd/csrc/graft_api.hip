@@ -9,6 +9,7 @@
 #include "graft_internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace graft {
 
@@ -39,6 +40,40 @@ SampleLayout sample_layout(graft_dtype dtype, int32_t batch, int32_t n_max, int3
   l.total = l.off_rec + align_up((size_t)batch * sizeof(SampleRec), 256);
   return l;
 }
+
+// Scratch of graft_tree_attention_noalloc (its split partials): one copy on
+// each device, looked up once per device with that device current.  Host
+// code uses only the looked-up address: the array's own name is a host-side
+// stand-in, not a device address.
+static __device__ __align__(256) unsigned char scratch[GRAFT_NOALLOC_SCRATCH_BYTES];
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+graft_status noalloc_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return set_error(GRAFT_ERR_HIP, "graft_tree_attention_noalloc: hipGetDevice: %s",
+                     hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(GRAFT_ERR_UNSUPPORTED, "graft_tree_attention_noalloc: device %d above %d",
+                     dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(GRAFT_ERR_HIP,
+                       "graft_tree_attention_noalloc: scratch lookup on device %d: %s", dev,
+                       hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GRAFT_OK;
+}
+}  // namespace
 
 }  // namespace graft
 
@@ -288,6 +323,34 @@ graft_status graft_tree_attention(graft_dtype dtype, int32_t batch, int32_t n_ma
                         max_prefix, sum_prefix, tree_mask, n_nodes, nullptr, nullptr, 0, scale,
                         out,
                         workspace, workspace_bytes, stream);
+}
+
+graft_status graft_tree_attention_noalloc(graft_dtype dtype, int32_t batch, int32_t n_max,
+                                          int32_t hq, int32_t hkv, int32_t head_dim,
+                                          const void *q, const void *k_tree,
+                                          const void *v_tree, const void *k_cache,
+                                          const void *v_cache, int32_t block_size,
+                                          const int32_t *block_table,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t *prefix_len, int32_t max_prefix,
+                                          int64_t sum_prefix, const uint32_t *tree_mask,
+                                          const int32_t *n_nodes, float scale, void *out,
+                                          hipStream_t stream) {
+  g_error[0] = 0;
+  graft_status st = check_attn_shape(dtype, batch, n_max, hq, hkv, head_dim, max_prefix);
+  if (st != GRAFT_OK) return st;
+  const AttnPlan pl =
+      plan_attention(dtype, batch, n_max, hq, hkv, head_dim, max_prefix, sum_prefix);
+  const size_t need = align_up(pl.part_o_bytes, 256) + align_up(pl.part_ml_bytes, 256);
+  REQUIRE(need <= GRAFT_NOALLOC_SCRATCH_BYTES, GRAFT_ERR_WORKSPACE,
+          "graft_tree_attention_noalloc: the plan needs %zu bytes of scratch, the library "
+          "holds %zu", need, (size_t)GRAFT_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != GRAFT_OK) return st;
+  return attention_impl(dtype, batch, n_max, hq, hkv, head_dim, q, k_tree, v_tree, k_cache,
+                        v_cache, block_size, block_table, max_blocks_per_seq, prefix_len,
+                        max_prefix, sum_prefix, tree_mask, n_nodes, nullptr, nullptr, 0, scale,
+                        out, ws, GRAFT_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 graft_status graft_tree_attention_rope(graft_dtype dtype, int32_t batch, int32_t n_max,
