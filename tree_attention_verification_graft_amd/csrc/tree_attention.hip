@@ -180,23 +180,21 @@ constexpr int kDmaPerStage = 4;          // per wave: 2 K + 2 V instructions
 // base + voffset (base wave-uniform, in SGPRs).  lds_base is the
 // wave-uniform LDS byte address of the 1 KB destination block.  The
 // non-temporal form is for tiles no other workgroup reads again.
+// The LDS address goes in as an M0 operand, so the compiler writes M0 itself
+// ahead of the instruction (it knows M0 is read here and clobbers nothing).
+// An M0 write needs one wait state before an LDS-DMA load, and the compiler's
+// hazard checks do not look inside inline assembly: hence the s_nop.
 __device__ __forceinline__ void dma16(const void *base, uint32_t voffset, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds_base), "v"(voffset), "s"(base)
-      : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voffset), "s"(base), "{m0}"(lds_base)
+               : "memory");
 }
 __device__ __forceinline__ void dma16_nt(const void *base, uint32_t voffset, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt"
-      :
-      : "s"(lds_base), "v"(voffset), "s"(base)
-      : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voffset), "s"(base), "{m0}"(lds_base)
+               : "memory");
 }
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
