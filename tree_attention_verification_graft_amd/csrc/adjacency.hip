@@ -31,6 +31,9 @@ constexpr int kThreads = 256;
 
 enum { kNPairs = 0, kNRows = 1, kSavedPairs = 2, kSavedRows = 3 };
 
+// Hash of a 64-bit key for the open-addressing tables: the 64-bit finalizer
+// ("fmix64") of Austin Appleby's public-domain MurmurHash3, with its published
+// shift amounts and multipliers.
 __device__ inline uint32_t hash32(uint64_t x) {
   x ^= x >> 33;
   x *= 0xff51afd7ed558ccdull;
