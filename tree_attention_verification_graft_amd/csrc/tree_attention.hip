@@ -182,16 +182,20 @@ constexpr int kDmaPerStage = 4;          // per wave: 2 K + 2 V instructions
 // non-temporal form is for tiles no other workgroup reads again.
 // The LDS address goes in as an M0 operand, so the compiler writes M0 itself
 // ahead of the instruction (it knows M0 is read here and clobbers nothing).
-// An M0 write needs one wait state before an LDS-DMA load, and the compiler's
-// hazard checks do not look inside inline assembly: hence the s_nop.
+// The compiler's hazard checks do not look inside inline assembly, so the
+// asm provides the wait states itself: the page base reaches its SGPR pair
+// through v_readfirstlane, and a vector-ALU write of an SGPR needs five wait
+// states before a vector-memory instruction reads it (an M0 write needs one
+// before an LDS-DMA load).  Without them the load can use the pair's stale
+// value as its address.
 __device__ __forceinline__ void dma16(const void *base, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voffset), "s"(base), "{m0}"(lds_base)
                : "memory");
 }
 __device__ __forceinline__ void dma16_nt(const void *base, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(voffset), "s"(base), "{m0}"(lds_base)
                : "memory");
