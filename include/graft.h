@@ -188,7 +188,11 @@ size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch,
  *   matrix_cores     1: the matrix-core kernel (bf16, head_dim 128, at least
  *                    16 query rows per KV head); 0: one wave per query row
  *   n_row_groups     workgroups along the query rows of one KV head
- *   rows_per_group   query rows (node x group + head-in-group) per row group
+ *   rows_per_group   query rows (node x group + head-in-group) of the largest
+ *                    row group.  Matrix-core plans cut the rows of a KV head
+ *                    into 16-row blocks, nb = ceil(n_max * group / 16), and
+ *                    give the first (nb mod n_row_groups) groups one block
+ *                    more than the others; the wavefront plan has one group
  *   n_splits         prefix splits; above 1 a combine launch merges them
  *   tiles_per_split  64-key prefix tiles per split
  *   tree_shift       split s covers prefix tiles [s tps - shift, (s+1) tps -

@@ -246,7 +246,17 @@ def plan_rows(w, tree, n_full_seqs, seed):
                                        int(w.prefix_len.sum()))
     _say(f"[parity] {w.name} plan: {plan}")
     Gq = w.Hq // w.Hkv
-    rpg = plan["rows_per_group"]
+    # row groups: runs of 16-row blocks, the first (blocks mod groups) one
+    # block longer (matrix-core plans); one group of all rows otherwise
+    ng = plan["n_row_groups"]
+    if plan["matrix_cores"]:
+        blocks = -(-(w.n_max * Gq) // 16)
+        lo, rem = divmod(blocks, ng)
+        bounds = [16 * (g * lo + min(g, rem)) for g in range(ng + 1)]
+    else:
+        bounds = [0, plan["rows_per_group"]]
+    assert max(b - a for a, b in zip(bounds, bounds[1:])) == plan["rows_per_group"]
+    group_of = lambda r: max(g for g in range(ng) if bounds[g] <= r)
     rng = np.random.default_rng(seed)
     nn = [int(x) for x in tree["n_nodes"]]
     rows = set()
@@ -258,14 +268,14 @@ def plan_rows(w, tree, n_full_seqs, seed):
     for b in range(w.B):
         rows.add((b, nn[b] - 1, int(rng.integers(w.Hq))))
         for h in range(w.Hkv):
-            for rg in range(plan["n_row_groups"]):
-                lo, hi = rg * rpg, min((rg + 1) * rpg, nn[b] * Gq)
+            for rg in range(ng):
+                lo, hi = bounds[rg], min(bounds[rg + 1], nn[b] * Gq)
                 if lo >= hi:
                     continue  # no rows of this sequence in the group
                 groups.add((b, h, rg))
                 r = int(rng.integers(lo, hi))
                 rows.add((b, r // Gq, h * Gq + r % Gq))
-    covered = {(b, h // Gq, (i * Gq + h % Gq) // rpg) for (b, i, h) in rows}
+    covered = {(b, h // Gq, group_of(i * Gq + h % Gq)) for (b, i, h) in rows}
     assert groups <= covered, "a workgroup set of the plan has no checked row"
     _say(f"[parity] {w.name}: {len(rows)} rows cover all {len(groups)} (sequence, KV head, "
          f"row group) sets x {plan['n_splits']} splits; every row of one KV head of "

@@ -286,6 +286,8 @@ static graft_status attention_impl(graft_dtype dtype, int32_t batch, int32_t n_m
   p.tiles_per_split = pl.tiles_per_split;
   p.n_row_groups = pl.n_row_groups;
   p.rows_per_group = pl.rows_per_group;
+  p.group_blocks_lo = pl.group_blocks_lo;
+  p.group_blocks_rem = pl.group_blocks_rem;
   p.lpt = pl.mfma && pl.lpt ? 1 : 0;
   p.key_pairs = pl.mfma && pl.key_pairs ? 1 : 0;
   p.tree_shift = pl.mfma ? pl.tree_shift : 0;

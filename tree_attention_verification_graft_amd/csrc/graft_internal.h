@@ -64,7 +64,11 @@ struct AttnParams {
   int32_t n_splits;        // prefix splits per (sequence, kv head, row group)
   int32_t tiles_per_split; // 64-key prefix tiles per split
   int32_t n_row_groups;    // row groups per (sequence, kv head)
-  int32_t rows_per_group;  // query rows per group (multiple of 16)
+  int32_t rows_per_group;  // query rows of the largest row group (multiple of 16)
+  // matrix-core path: row groups are runs of 16-row blocks, the first
+  // group_blocks_rem of them group_blocks_lo + 1 blocks long, the rest
+  // group_blocks_lo (the wavefront path has one group of rows_per_group rows)
+  int32_t group_blocks_lo, group_blocks_rem;
   int32_t lpt;             // rank (sequence, split) pairs longest first on the device
   int32_t key_pairs;       // waves w and w + 4 share rows, one 32-key half of each tile each
   int32_t tree_shift;      // split s covers prefix tiles [s tps - shift, (s + 1) tps - shift)
@@ -77,6 +81,7 @@ struct AttnPlan {
   bool key_pairs;  // at most 4 row blocks per group: waves pair up on the keys of each tile
   int32_t tree_shift;  // tree tiles counted at the front of split 0 (0: none)
   int32_t n_splits, tiles_per_split, n_row_groups, rows_per_group;
+  int32_t group_blocks_lo, group_blocks_rem;  // see AttnParams
   size_t part_o_bytes, part_ml_bytes;
 };
 // sum_prefix: the caller's sum of prefix lengths (<= 0: unknown, every

@@ -125,6 +125,19 @@ __device__ inline int active_splits(const AttnParams &p, int nt_prefix) {
              max(1, (nt_prefix + p.tree_shift + p.tiles_per_split - 1) / p.tiles_per_split));
 }
 
+// First query row of row group rg, and the row group holding query row r
+// (matrix-core path: the first group_blocks_rem groups hold one 16-row block
+// more than the others, so that no two groups differ by more than a block).
+__device__ inline int group_row0(const AttnParams &p, int rg) {
+  return 16 * (rg * p.group_blocks_lo + min(rg, p.group_blocks_rem));
+}
+__device__ inline int group_of_row(const AttnParams &p, int r) {
+  if (p.n_row_groups == 1) return 0;
+  const int blk = r >> 4, big = p.group_blocks_rem * (p.group_blocks_lo + 1);
+  return blk < big ? blk / (p.group_blocks_lo + 1)
+                   : p.group_blocks_rem + (blk - big) / p.group_blocks_lo;
+}
+
 // LDS row of the K tile that holds key `k` (0..63) of the tile.  Rows are in
 // the order the transposed score blocks use: score block kb = 2*kp + half,
 // row 4*g + i holds key 32*kp + 8*g + 4*half + i.
@@ -246,7 +259,7 @@ struct MfmaCtx {
 // One wave's share, specialised on the number NA of 16-row query blocks it
 // owns (wave-uniform), so that no matrix instruction sits behind a per-block
 // branch.  Every wave runs the same loads and barriers whatever NA is.
-template <int NA, bool ROPE, bool PAIR>
+template <int NA, bool ROPE, bool PAIR, bool NT>
 __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCtx &c,
                                                uint8_t *smem, int32_t *s_tpos) {
   constexpr int NQ = NA > 0 ? NA : 1;
@@ -354,10 +367,10 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   auto tile_page = [&](int it) {
     return table[(uint32_t)min((c.t_begin + it) * 4 + my_page, last_page)];
   };
-  // With one row group no other workgroup reads a tile again, so the tiles
-  // stream past the caches; several row groups re-read each other's tiles
-  // through L2.
-  const bool read_once = p.n_row_groups == 1;
+  // NT (plans with one row group): no other workgroup reads a tile again,
+  // so the tiles stream past the caches; several row groups re-read each
+  // other's tiles through L2.  A template parameter rather than a runtime
+  // test, which would split the tile loop's basic blocks.
   auto issue_prefix = [&](int st, int blk) {
     // the page base is wave-uniform; read it from lane 0 so that it stays in
     // SGPRs for the asm operand whatever the register pressure around it
@@ -369,7 +382,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     const char *base =
         reinterpret_cast<const char *>(((uint64_t)ba_hi << 32) | (uint64_t)ba_lo);
     const uint32_t sbase = c.lds0 + st * kStageBytes;
-    if (read_once) {
+    if constexpr (NT) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) dma16_nt(base, dma_off[q], sbase + dma_dst(q));
     } else {
@@ -847,7 +860,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   }
 }
 
-template <int NB, bool ROPE, bool LPT>
+template <int NB, bool ROPE, bool LPT, bool NT>
 __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   __shared__ int32_t s_tpos[ROPE ? GRAFT_MAX_NODES : 1];  // tree positions (rotary path)
@@ -915,7 +928,7 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
     const int32_t *tp = p.tree_pos + (size_t)c.b * p.n_max;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int r = c.rg * p.rows_per_group + 16 * (c.wslot + c.wstride * k) + (c.lane & 15);
+      const int r = group_row0(p, c.rg) + 16 * (c.wslot + c.wstride * k) + (c.lane & 15);
       c.qpos[k] = tp[min(r / p.group, p.n_max - 1)];
     }
     c.tpos = c.tid < p.n_max ? tp[c.tid] : 0;
@@ -941,7 +954,8 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
   c.P = min(max(p.prefix_len[c.b], 0), p.max_blocks * kBlock);
   c.G = p.group;
   c.rows_b = c.n_nodes * c.G;
-  c.row0 = c.rg * p.rows_per_group;
+  c.row0 = group_row0(p, c.rg);
+  const int group_rows = 16 * (p.group_blocks_lo + (c.rg < p.group_blocks_rem ? 1 : 0));
   if (c.row0 >= c.rows_b) return;  // group past this sequence's rows
 
   const int nt_prefix = (c.P + kTile - 1) / kTile;
@@ -959,17 +973,17 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     const int rl = 16 * (c.wslot + c.wstride * k);
-    if (rl < p.rows_per_group && c.row0 + rl < c.rows_b) na = k + 1;
+    if (rl < group_rows && c.row0 + rl < c.rows_b) na = k + 1;
   }
-  if (NB >= 3 && na == 3) mfma_wave_body<3, ROPE, false>(p, c, smem, s_tpos);
-  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1), ROPE, false>(p, c, smem, s_tpos);
+  if (NB >= 3 && na == 3) mfma_wave_body<3, ROPE, false, NT>(p, c, smem, s_tpos);
+  else if (NB >= 2 && na == 2) mfma_wave_body<(NB >= 2 ? 2 : 1), ROPE, false, NT>(p, c, smem, s_tpos);
   else if (na == 1) {
-    if (pair) mfma_wave_body<1, ROPE, true>(p, c, smem, s_tpos);
-    else mfma_wave_body<1, ROPE, false>(p, c, smem, s_tpos);
+    if (pair) mfma_wave_body<1, ROPE, true, NT>(p, c, smem, s_tpos);
+    else mfma_wave_body<1, ROPE, false, NT>(p, c, smem, s_tpos);
   } else if (pair) {
-    mfma_wave_body<0, ROPE, true>(p, c, smem, s_tpos);
+    mfma_wave_body<0, ROPE, true, NT>(p, c, smem, s_tpos);
   } else {
-    mfma_wave_body<0, ROPE, false>(p, c, smem, s_tpos);
+    mfma_wave_body<0, ROPE, false, NT>(p, c, smem, s_tpos);
   }
 }
 
@@ -1121,10 +1135,16 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------------
 // Combine: merge the prefix splits of one output row (log-sum-exp in base 2).
-// One wave per row, no barriers: lane s reads split s's (max, sum), the
-// wave reduces them, and each lane accumulates two head dims over the
-// splits, taking split j's weight from lane j with a scalar read-lane.
+// Two forms.  Launches with few output rows (and often many splits) take one
+// wave per row: lane s reads split s's (max, sum), the wave reduces them, and
+// each lane accumulates two head dims over the splits, taking split j's
+// weight from lane j with a scalar read-lane.  Launches with many output
+// rows and few splits take sixteen lanes per row, each owning head_dim / 16
+// dims and folding the splits' (max, sum) pairs itself (the same addresses
+// for the row's lanes), so that no cross-lane reduction is needed and each
+// split's partial row is one contiguous read.
 constexpr int kMaxSplits = 256;
+constexpr int kCombineManyRows = 8192;  // output rows from which the 16-lane form pays
 
 __device__ inline float wave_max(float x) {
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -1136,7 +1156,7 @@ __device__ inline float wave_sum(float x) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) void attn_combine_wave_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int hq = (int)(row % p.hq);
@@ -1146,8 +1166,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int G = p.group;
   const int h = hq / G;
   const int r = node * G + hq % G;
-  const int rg = r / p.rows_per_group;
-  const int rl = r % p.rows_per_group;
+  const int rg = group_of_row(p, r);
+  const int rl = p.n_row_groups == 1 ? r : r - group_row0(p, rg);
   const int P = min(max(p.prefix_len[b], 0), p.max_blocks * kBlock);
   const int nt_prefix = (P + kTile - 1) / kTile;
   const int active = active_splits(p, nt_prefix);
@@ -1225,6 +1245,73 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   } else {
     out[lane] = (T)(acc0 * inv);
   }
+}
+
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_combine_rows_kernel(AttnParams p) {
+  constexpr int DPL = D / 16;  // dims per lane: 8 or 4
+  const int ln = threadIdx.x & 15;
+  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int hq = (int)(row % p.hq);
+  const int node = (int)((row / p.hq) % p.n_max);
+  const int b = (int)(row / ((long)p.hq * p.n_max));
+  if (b >= p.batch || node >= min(p.n_nodes[b], p.n_max)) return;  // a row's lanes together
+  const int G = p.group;
+  const int h = hq / G;
+  const int r = node * G + hq % G;
+  const int rg = group_of_row(p, r);
+  const int rl = p.n_row_groups == 1 ? r : r - group_row0(p, rg);
+  const int P = min(max(p.prefix_len[b], 0), p.max_blocks * kBlock);
+  const int nt_prefix = (P + kTile - 1) / kTile;
+  const int active = active_splits(p, nt_prefix);
+  if (active == 1) return;  // written by the attention kernel
+  const size_t base = (((size_t)b * p.hkv + h) * p.n_row_groups + rg) * p.n_splits;
+  const size_t stride = (size_t)p.rows_per_group;  // partial rows between splits
+  const float *ml = p.part_ml + (base * stride + rl) * 2;
+  const float *po = p.part_o + (base * stride + rl) * D + DPL * ln;
+  float M = kNegBig;
+  for (int j = 0; j < active; ++j) M = fmaxf(M, ml[(size_t)j * stride * 2]);
+  float L = 0.f, acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  const size_t sstride = stride * D;  // floats between splits
+  auto load = [&](float (&x)[DPL], const float *src) {
+#pragma unroll
+    for (int q = 0; q < DPL / 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4 *>(src + 4 * q);
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+  };
+  int j = 0;
+  for (; j + 4 <= active; j += 4) {
+    float x[4][DPL], mj[4], lj[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      load(x[u], po + (size_t)(j + u) * sstride);
+      mj[u] = ml[(size_t)(j + u) * stride * 2];
+      lj[u] = ml[(size_t)(j + u) * stride * 2 + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = fast_exp2(mj[u] - M);
+      L += w * lj[u];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += w * x[u][e];
+    }
+  }
+  for (; j < active; ++j) {
+    float x[DPL];
+    load(x, po + (size_t)j * sstride);
+    const float w = fast_exp2(ml[(size_t)j * stride * 2] - M);
+    L += w * ml[(size_t)j * stride * 2 + 1];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += w * x[e];
+  }
+  const float inv = 1.f / L;
+  T *out = static_cast<T *>(p.out) + (((size_t)b * p.n_max + node) * p.hq + hq) * D + DPL * ln;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) out[e] = (T)(acc[e] * inv);
 }
 
 }  // namespace
@@ -1338,6 +1425,8 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
           best = t;
           pl.n_row_groups = groups;
           pl.rows_per_group = 16 * bpg;
+          pl.group_blocks_lo = blocks / groups;
+          pl.group_blocks_rem = blocks % groups;
           pl.tiles_per_split = tps;
           pl.n_splits = splits;
           pl.key_pairs = pairs;
@@ -1359,6 +1448,7 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
   } else {
     pl.n_row_groups = 1;
     pl.rows_per_group = (rows + 3) / 4 * 4;
+    pl.group_blocks_lo = pl.group_blocks_rem = 0;
     const long base = (long)batch * hkv * (pl.rows_per_group / 4);
     int splits = (int)max(1L, min((long)tiles, (512 + base - 1) / max(1L, base)));
     splits = min(min(splits, max(1, tiles / 4)), kMaxSplits);
@@ -1374,12 +1464,19 @@ AttnPlan plan_attention(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t
 namespace {
 template <int NB>
 void launch_mfma(const AttnParams &p, dim3 grid, hipStream_t stream) {
-  const int kind = (p.rope ? 1 : 0) + (p.lpt ? 2 : 0);
+  // non-temporal tile loads when no other row group re-reads the tiles
+  const bool nt = p.n_row_groups == 1;
+  const int kind = (p.rope ? 1 : 0) + (p.lpt ? 2 : 0) + (nt ? 4 : 0);
+  const dim3 block(kMfmaThreads);
   switch (kind) {
-    case 0: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, false>), grid, dim3(kMfmaThreads), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, false>), grid, dim3(kMfmaThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, true>), grid, dim3(kMfmaThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, true>), grid, dim3(kMfmaThreads), 0, stream, p); break;
+    case 0: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, false, false>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, false, false>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, true, false>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, true, false>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, false, true>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, false, true>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((attn_mfma_kernel<NB, false, true, true>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_mfma_kernel<NB, true, true, true>), grid, block, 0, stream, p); break;
   }
 }
 }  // namespace
@@ -1424,13 +1521,26 @@ void launch_attention_wave(graft_dtype dtype, const AttnParams &p, hipStream_t s
   }
 }
 
+namespace {
+template <typename T>
+void launch_combine(const AttnParams &p, long rows, hipStream_t stream) {
+  if (rows >= kCombineManyRows) {
+    dim3 grid((unsigned)((rows + 15) / 16));
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL((attn_combine_rows_kernel<T, 128>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_combine_rows_kernel<T, 64>), grid, dim3(256), 0, stream, p);
+  } else {
+    dim3 grid((unsigned)((rows + 3) / 4));
+    hipLaunchKernelGGL(attn_combine_wave_kernel<T>, grid, dim3(256), 0, stream, p);
+  }
+}
+}  // namespace
+
 void launch_attention_combine(graft_dtype dtype, const AttnParams &p, hipStream_t stream) {
   const long rows = (long)p.batch * p.n_max * p.hq;
-  dim3 grid((unsigned)((rows + 3) / 4));
-  if (dtype == GRAFT_F32)
-    hipLaunchKernelGGL(attn_combine_kernel<float>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel<__hip_bfloat16>, grid, dim3(256), 0, stream, p);
+  if (dtype == GRAFT_F32) launch_combine<float>(p, rows, stream);
+  else launch_combine<__hip_bfloat16>(p, rows, stream);
 }
 
 }  // namespace graft
