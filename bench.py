@@ -17,6 +17,9 @@ that fits one GPU.  The same run also times the attention call alone at the
 three bf16 8B-model shapes (llama3_8b_b1, qwen3_8b_b16, llama31_8b_64k) and
 reports their KV-read bandwidth against the HBM peak.
 
+  --no-extras          skip the attention-only timings at the other 8B shapes
+                       (profiler runs of one workload)
+
 Counter support (HBM traffic of the attention call, see profiles/):
   --copy-calibration   after the timed steps, run a plain elementwise copy of
                        256 MiB three times, so that a rocprofv3 --pmc pass over
@@ -267,6 +270,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the attention timings at the other 8B-model shapes")
     ap.add_argument("--traffic-from-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.traffic_from_pmc:
@@ -371,7 +376,7 @@ def main():
     # the bound, in the same process
     shapes_8b = {}
     for name in ATTN_8B_SHAPES:
-        if name == w.name:
+        if name == w.name or args.no_extras:
             continue
         shapes_8b[name] = attention_only(name, dev, stream, reps)
         log(f"{name}: attention {shapes_8b[name]['attention_us']:.1f} us, "
