@@ -87,9 +87,17 @@ __device__ inline float pos_inf() {
 __device__ inline float fmax2(float a, float b, float inf) {
   return __builtin_amdgcn_fmed3f(a, b, inf);
 }
-__device__ inline float max8(const f32x4 &a, const f32x4 &b, float inf) {
-  return fmax2(fmax2(fmax2(a[0], a[1], inf), fmax2(a[2], a[3], inf), inf),
-               fmax2(fmax2(b[0], b[1], inf), fmax2(b[2], b[3], inf), inf), inf);
+// Maximum of eight scores (finite or -inf): the IEEE maximum operation,
+// which gfx950 evaluates three inputs at a time (v_maximum3_f32), four
+// instructions where a chain of two-input maxima takes seven.
+__device__ inline float max8(const f32x4 &a, const f32x4 &b, float) {
+  float m = __builtin_elementwise_maximum(a[0], a[1]);
+  m = __builtin_elementwise_maximum(m, a[2]);
+  m = __builtin_elementwise_maximum(m, a[3]);
+  m = __builtin_elementwise_maximum(m, b[0]);
+  m = __builtin_elementwise_maximum(m, b[1]);
+  m = __builtin_elementwise_maximum(m, b[2]);
+  return __builtin_elementwise_maximum(m, b[3]);
 }
 
 // Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
