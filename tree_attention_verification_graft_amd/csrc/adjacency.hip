@@ -366,12 +366,12 @@ __global__ __launch_bounds__(kThreads) void reselect_kernel(UpdateParams p) {
 
 // ---------------------------------------------------------------------------
 // Small calls (at most kSmallT potential transitions, the per-step case).
-// Every workgroup of the launch gathers the valid (u, v) keys into LDS,
-// sorts them (equal pairs form runs whose length is the count; each row is
-// one segment) and numbers the rows in sorted order; workgroup g then merges
-// rows g, g + G, ... with one wave per row.  The row numbering depends only
-// on the sorted keys, so all workgroups agree on it, and the table needs no
-// workspace.
+// Rows are partitioned over the workgroups by source token: workgroup g owns
+// the rows u with u mod G = g.  Each workgroup gathers the valid (u, v) keys
+// of its own rows into LDS, sorts them (equal pairs form runs whose length
+// is the count; each row is one segment), numbers its rows in sorted order
+// and merges them with one wave per row.  No two workgroups touch the same
+// row, so they need no agreement, and the table needs no workspace.
 constexpr int kSmallT = 4096;
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
@@ -394,24 +394,39 @@ __global__ __launch_bounds__(kSmallThreads) void update_small_kernel(UpdateParam
   const int lane = tid & 63, wave = tid >> 6;
   const unsigned long long kNone = ~0ull;
 
-  // 1) gather the valid (u, v) keys (in any order: they are sorted next)
+  // 1) gather the valid (u, v) keys of this workgroup's rows (in any order:
+  // they are sorted next)
   if (tid == 0) s_nv = 0;
   __syncthreads();
+  // kGather transitions per thread per round, every load of a round issued
+  // before any is used: for t < max_transitions = n_paths * (path_stride -
+  // 1), the path index is below n_paths and k + 1 below path_stride, so the
+  // token reads stay inside the path array whatever accept_len holds
+  constexpr int kGather = 4;
   const int per = p.path_stride - 1;
-  for (int t0 = 0; t0 < p.max_transitions; t0 += kSmallThreads) {
-    const int t = t0 + tid;
-    unsigned long long key = kNone;
-    if (t < p.max_transitions) {
-      const int path = t / per, k = t % per;
-      const int L = p.accept_len[path];
-      if (L >= 0 && k <= L && L + 2 <= p.path_stride) {
-        const int u = p.path_tokens[(size_t)path * p.path_stride + k];
-        const int v = p.path_tokens[(size_t)path * p.path_stride + k + 1];
-        if (u >= 0 && u < p.vocab && v >= 0 && v < p.vocab)
-          key = ((unsigned long long)(uint32_t)u << 32) | (uint32_t)v;
+  for (int t0 = 0; t0 < p.max_transitions; t0 += kSmallThreads * kGather) {
+    int L[kGather], u[kGather], v[kGather], k[kGather];
+#pragma unroll
+    for (int j = 0; j < kGather; ++j) {
+      const int t = t0 + j * kSmallThreads + tid;
+      L[j] = -1;
+      u[j] = v[j] = k[j] = 0;
+      if (t < p.max_transitions) {
+        const int path = t / per;
+        k[j] = t % per;
+        L[j] = p.accept_len[path];
+        u[j] = p.path_tokens[(size_t)path * p.path_stride + k[j]];
+        v[j] = p.path_tokens[(size_t)path * p.path_stride + k[j] + 1];
       }
     }
-    if (key != kNone) s_key[atomicAdd(&s_nv, 1)] = key;
+#pragma unroll
+    for (int j = 0; j < kGather; ++j) {
+      if (L[j] >= 0 && k[j] <= L[j] && L[j] + 2 <= p.path_stride && u[j] >= 0 &&
+          u[j] < p.vocab && v[j] >= 0 && v[j] < p.vocab &&
+          (uint32_t)u[j] % gridDim.x == blockIdx.x)
+        s_key[atomicAdd(&s_nv, 1)] =
+            ((unsigned long long)(uint32_t)u[j] << 32) | (uint32_t)v[j];
+    }
   }
   __syncthreads();
   const int nv = s_nv;
@@ -474,10 +489,9 @@ __global__ __launch_bounds__(kSmallThreads) void update_small_kernel(UpdateParam
   if (tid == 0) s_row_beg[n_rows] = (uint16_t)nv;
   __syncthreads();
 
-  // 4) rows g, g + G, ... of this workgroup, one wave each
+  // 4) this workgroup's rows, one wave each
   const int S = p.top_s;
-  const int G = gridDim.x;
-  for (int r = blockIdx.x + G * wave; r < n_rows; r += G * kSmallWaves) {
+  for (int r = wave; r < n_rows; r += kSmallWaves) {
     const int beg = s_row_beg[r];
     const int end = s_row_beg[r + 1];
     const int u = (int)(s_key[beg] >> 32);
