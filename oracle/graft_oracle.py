@@ -572,7 +572,9 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
     `margin_bonus`, the distance of the bonus draw's target from the nearest
     boundary of the sampled token's CDF interval, relative to the residual
     mass.  An implementation whose probabilities carry an error below a
-    margin takes the same decision."""
+    margin takes the same decision.  `margin_by_depth[b][d]` is the smallest
+    child-test margin among the tests at the path's node of depth d (inf
+    where none was made): decisions before the first close one are certain."""
     lg = as_f64(np.asarray(logits), dtype)
     B, n_max, V = lg.shape
     T = float(temperature)
@@ -581,6 +583,7 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
     path_tokens = np.full((B, n_max + 1), -1, np.int32)
     margin_accept = np.full(B, np.inf)
     margin_bonus = np.full(B, np.inf)
+    margin_by_depth = np.full((B, n_max), np.inf)
     for b in range(B):
         n = int(n_nodes[b])
         node = 0
@@ -601,6 +604,8 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
                 thr = p[x] / (1.0 - removed) if removed < 1.0 else 0.0
                 u = float(rand_accept[b, c])
                 margin_accept[b] = min(margin_accept[b], abs(u * (1.0 - removed) - p[x]))
+                d = len(path) - 1
+                margin_by_depth[b, d] = min(margin_by_depth[b, d], abs(u * (1.0 - removed) - p[x]))
                 if u < thr:
                     nxt = c
                     break
@@ -627,4 +632,4 @@ def accept_sample(logits, dtype: str, temperature: float, tree_token, tree_paren
         path_tokens[b, len(path)] = bonus
     return {"accept_len": accept_len, "path_nodes": path_nodes,
             "path_tokens": path_tokens, "margin_accept": margin_accept,
-            "margin_bonus": margin_bonus}
+            "margin_bonus": margin_bonus, "margin_by_depth": margin_by_depth}

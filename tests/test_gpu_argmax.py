@@ -5,8 +5,8 @@ The argmax is the lowest index among the maxima, with -0 equal to +0
 the "Draft Less, Retrieve More" summary).  Random logits almost never tie,
 so these rows plant the cases that decide ties: repeated maxima in one chunk
 and across chunks, signed zeros as the maximum, all-negative rows, the
-extreme finite values, constant rows, and maxima at the first and last
-vocabulary entries.  Both chunk sizes of the argmax launch are covered
+extreme finite values, constant rows, maxima at the first and last
+vocabulary entries, and equal maxima on both sides of a chunk edge.  Both chunk sizes of the argmax launch are covered
 (a small grid, and one above 8192 workgroups).
 """
 import numpy as np
@@ -25,7 +25,7 @@ def _rows(n_rows, V, seed):
     rng = np.random.default_rng(seed)
     out = np.empty((n_rows, V), np.uint16)
     for r in range(n_rows):
-        case = r % 9
+        case = r % 10
         x = rng.standard_normal(V).astype(np.float32)
         bits = W.f32_to_bf16_bits(x)
         if case == 0:  # one maximum, planted three times (two near, one far)
@@ -51,6 +51,12 @@ def _rows(n_rows, V, seed):
         elif case == 6:  # extreme finite values: -max everywhere but one +max
             bits[:] = 0xFF7F
             bits[int(rng.integers(V))] = 0x7F7F
+        elif case == 9:  # one maximum on both sides of each chunk edge (4096- and
+            # 6144-entry chunks): the lower index, in the earlier chunk, wins
+            m = W.f32_to_bf16_bits(np.array([15.0], np.float32))[0]
+            for edge in (6144, 4096):
+                if edge < V:
+                    bits[edge - 1] = bits[edge] = m
         elif case == 7:  # a constant negative row: entry 0
             bits[:] = W.f32_to_bf16_bits(np.array([-3.0], np.float32))[0]
         else:  # only -max: entry 0

@@ -61,6 +61,17 @@ def compare(ref, got, parent, token, n_nodes, V, max_ambiguous_frac=0.05):
             np.testing.assert_array_equal(path_tokens[b], ref["path_tokens"][b])
         else:
             amb += 1
+            # the decisions before the first close one are certain: the paths
+            # agree up to the node where it was taken, and all the way when
+            # only the bonus draw is close (then only the bonus may differ)
+            close = np.nonzero(ref["margin_by_depth"][b] <= MARGIN_ACCEPT)[0]
+            d = int(close[0]) if len(close) else int(ref["accept_len"][b])
+            np.testing.assert_array_equal(path_nodes[b, :d + 1], ref["path_nodes"][b, :d + 1])
+            if not len(close):
+                assert int(acc_len[b]) == int(ref["accept_len"][b]), b
+                np.testing.assert_array_equal(path_nodes[b], ref["path_nodes"][b])
+                np.testing.assert_array_equal(path_tokens[b, :d + 1],
+                                              ref["path_tokens"][b, :d + 1])
     assert amb <= max(1, int(max_ambiguous_frac * B)), f"{amb} of {B} sequences ambiguous"
     return amb
 

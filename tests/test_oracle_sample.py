@@ -144,3 +144,32 @@ def test_margins_on_a_hand_worked_case():
     # float32 logits of log(p) carry ~1e-8 relative error
     assert abs(r["margin_accept"][0] - 0.02) < 1e-6
     assert abs(r["margin_bonus"][0] - 0.1) < 1e-6
+    # both child tests are made at the root (depth 0); node 2 makes none
+    md = r["margin_by_depth"][0]
+    assert abs(md[0] - 0.02) < 1e-6 and np.isinf(md[1:]).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_margin_by_depth_places_each_test_on_the_path(seed):
+    """The per-depth margins cover exactly the nodes of the path that made a
+    child test, and their minimum is the sequence's margin_accept."""
+    rng = np.random.default_rng(seed)
+    B, n, V = 6, 12, 7
+    parent = np.full((B, n), -1, np.int32)
+    for b in range(B):
+        for i in range(1, n):
+            parent[b, i] = int(rng.integers(0, i))
+    token = rng.integers(0, V, (B, n)).astype(np.int32)
+    logits = (rng.standard_normal((B, n, V)) * 2.0).astype(np.float32)
+    ra = rng.random((B, n))
+    rs = rng.random((B, n))
+    r = O.accept_sample(logits, "f32", 0.7, token, parent, np.full(B, n), ra, rs)
+    for b in range(B):
+        L = int(r["accept_len"][b])
+        md = r["margin_by_depth"][b]
+        path = r["path_nodes"][b, :L + 1]
+        for d in range(n):
+            has_child = d <= L and any(int(parent[b, c]) == int(path[d]) for c in range(n))
+            assert np.isfinite(md[d]) == has_child, (b, d)
+        assert np.min(md) == r["margin_accept"][b]
+
