@@ -47,7 +47,7 @@ def check_tree(gpu, ref):
     np.testing.assert_array_equal(gpu["mask"], ref["mask"])
 
 
-def check_attention(w, out_gpu, tree, rows=None):
+def check_attention(w, out_gpu, tree, rows=None, raw_bar=True):
     from tree_attention_verification_graft_amd.pipeline import to_host
     got = _f64(to_host(out_gpu), w.dtype)
     ref = O.tree_attention(_f64(w.q, w.dtype), _f64(w.k_tree, w.dtype), _f64(w.v_tree, w.dtype),
@@ -64,12 +64,14 @@ def check_attention(w, out_gpu, tree, rows=None):
          f"beyond output rounding {excess:.3e} (bar {TOL[w.dtype]})")
     # the bar on the plain max-abs error, and the same bar on what is left
     # after the output's own rounding to its storage type
-    assert np.isfinite(err) and err <= TOL[w.dtype], f"attention max-abs {err}"
+    assert np.isfinite(err), f"attention max-abs {err}"
+    if raw_bar:
+        assert err <= TOL[w.dtype], f"attention max-abs {err}"
     assert excess <= TOL[w.dtype], f"attention error beyond output rounding {excess}"
     return err
 
 
-def run_full_check(w, attn_rows=None, seed_prompt=False):
+def run_full_check(w, attn_rows=None, seed_prompt=False, raw_bar=True):
     """Whole step on the GPU vs the oracle: build, attention, accept (with a
     planted path), update, and the commit of the accepted path to the cache."""
     import torch
@@ -94,7 +96,7 @@ def run_full_check(w, attn_rows=None, seed_prompt=False):
     check_tree(ds.tree_host(), ref_tree)
     ds.attention()
     torch.cuda.synchronize()
-    err = check_attention(w, ds.out, ref_tree, rows=attn_rows)
+    err = check_attention(w, ds.out, ref_tree, rows=attn_rows, raw_bar=raw_bar)
     ds.accept()
     torch.cuda.synchronize()
     ref_acc = O.accept(logits, w.dtype, ref_tree["token"], ref_tree["parent"],
