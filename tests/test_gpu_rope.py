@@ -190,3 +190,13 @@ def test_unit_table_equals_the_unrotated_call():
     ds.attention_rope()
     torch.cuda.synchronize()
     assert torch.equal(plain.view(torch.int16), ds.out.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------
+# seeded random shapes (tests/random_shapes.py): every third case
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", range(0, 24, 3))
+def test_random_shape(case):
+    import random_shapes as R
+    _run(R.make_case(case))

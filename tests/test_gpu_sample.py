@@ -258,3 +258,22 @@ def test_full_size(name):
     ref = oracle_sample(logits, w.dtype, 1.0, t["token"], t["parent"], t["n_nodes"], ra, rs)
     amb = compare(ref, got, t["parent"], t["token"], t["n_nodes"], w.V)
     _say(f"[sample] {name} full size: ok, accept_len {got[0].tolist()[:8]}, ambiguous {amb}")
+
+
+# ----------------------------------------------------------------------------
+# seeded random shapes (tests/random_shapes.py): every third case, from the
+# second on, trees from the build call
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", range(1, 24, 3))
+def test_random_shape(case):
+    import random_shapes as R
+    w = R.make_case(case)
+    ds, t = _built_tree(w)
+    logits = W.plant_path(w.logits, w.dtype, t["token"], t["parent"], t["n_nodes"],
+                          w.plant_seed, boost=4.0)
+    ra, rs = W.sampling_uniforms(500 + case, w.B, ds.n_max)
+    got = run_sample(logits, w.dtype, 1.0, t["token"], t["parent"], t["n_nodes"], ra, rs)
+    ref = oracle_sample(logits, w.dtype, 1.0, t["token"], t["parent"], t["n_nodes"], ra, rs)
+    amb = compare(ref, got, t["parent"], t["token"], t["n_nodes"], w.V)
+    _say(f"[sample] random case {case}: ok, accept_len {got[0].tolist()[:8]}, ambiguous {amb}")
