@@ -333,11 +333,14 @@ UPDATE_TREE = [(n, SMALL[n]) for n in W.CONFIG_ORDER] + [
 @pytest.mark.parametrize("name,over", UPDATE_TREE,
                          ids=[f"{n}-{i}" for i, (n, _) in enumerate(UPDATE_TREE)])
 def test_update_tree_small_variant(name, over):
+    run_update_tree_check(W.make(name, **over))
+
+
+def run_update_tree_check(w):
     """The all-node update on the GPU against the oracle, from the same M:
     every verified node's (token, argmax) transition."""
     import torch
     from tree_attention_verification_graft_amd.pipeline import DeviceStep, to_host
-    w = W.make(name, **over)
     m_ids, m_scores = w.m_ids, w.m_scores
     if w.prompt is not None:
         m_ids, m_scores = O.update_adjacency(m_ids, m_scores, w.prompt[None],

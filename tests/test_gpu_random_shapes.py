@@ -20,7 +20,7 @@ here; the named workloads, whose long prefixes keep |out| small, assert it.
 import pytest
 
 import random_shapes as R
-from test_gpu_parity import run_full_check
+from test_gpu_parity import run_full_check, run_update_tree_check
 
 pytestmark = pytest.mark.gpu
 
@@ -28,3 +28,10 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("case", range(R.N_CASES))
 def test_random_shape(case):
     run_full_check(R.make_case(case), raw_bar=False)
+
+
+@pytest.mark.parametrize("case", range(2, R.N_CASES, 3))
+def test_random_shape_update_tree(case):
+    """The all-node update of M (every verified node's transition)."""
+    run_update_tree_check(R.make_case(case))
+
