@@ -16,7 +16,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on the GPU machine only; on a machine without a GPU they are
+    # GPU tests need an MI355X; on a machine without a GPU they are
     # skipped rather than failed so that `-m "not gpu"` and plain runs agree.
     try:
         import torch
