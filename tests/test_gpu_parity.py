@@ -325,8 +325,11 @@ def test_literal_k_ret_order_full_size():
 
 
 UPDATE_TREE = [(n, SMALL[n]) for n in W.CONFIG_ORDER] + [
-    # more than 1024 verified nodes: the hash-table path of the update
+    # 1040 verified nodes: the per-step path with many rows per workgroup
     ("qwen3_8b_b16", dict(B=16, Hq=8, Hkv=2, prefix=(40, 300), V=4096)),
+    # 4160 potential transitions, above the per-step path's 4096: the
+    # hash-table path of the update
+    ("qwen3_8b_b16", dict(B=64, Hq=4, Hkv=1, prefix=(20, 60), V=4096)),
 ]
 
 

@@ -564,8 +564,8 @@ UpdateLayout update_layout(uint32_t capacity) {
   return l;
 }
 
-void launch_update(const UpdateParams &p, hipStream_t stream, int32_t small_limit) {
-  if (p.max_transitions <= std::min(small_limit, kSmallT)) {
+void launch_update(const UpdateParams &p, hipStream_t stream) {
+  if (p.max_transitions <= kSmallT) {
     // enough workgroups that every touched row (at most one per transition)
     // gets a wave of its own
     const int groups = std::max(1, std::min(64, (p.max_transitions + kSmallWaves - 1) / kSmallWaves));

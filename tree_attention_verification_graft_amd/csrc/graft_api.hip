@@ -512,8 +512,7 @@ size_t graft_update_adjacency_workspace_size(int32_t n_paths, int32_t path_strid
 static graft_status update_impl(int32_t *m_ids, float *m_scores, int32_t vocab, int32_t top_s,
                                 int32_t n_paths, int32_t path_stride,
                                 const int32_t *path_tokens, const int32_t *accept_len,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream,
-                                int32_t small_limit) {
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
   g_error[0] = 0;
   REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_update_adjacency: vocab < 1");
   REQUIRE(top_s >= 1 && top_s <= GRAFT_MAX_TOP_S, GRAFT_ERR_INVALID_ARG,
@@ -546,7 +545,7 @@ static graft_status update_impl(int32_t *m_ids, float *m_scores, int32_t vocab, 
   p.accept_len = accept_len;
   p.ws = static_cast<char *>(workspace);
   p.lay = update_layout(cap);
-  launch_update(p, stream, small_limit);
+  launch_update(p, stream);
   return check_launch("graft_update_adjacency");
 }
 
@@ -556,7 +555,7 @@ graft_status graft_update_adjacency(int32_t *m_ids, float *m_scores, int32_t voc
                                     void *workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
   return update_impl(m_ids, m_scores, vocab, top_s, n_paths, path_stride, path_tokens,
-                     accept_len, workspace, workspace_bytes, stream, 4096);
+                     accept_len, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------------- all-node update
@@ -598,10 +597,12 @@ graft_status graft_update_adjacency_tree(int32_t *m_ids, float *m_scores, int32_
   const graft_status st = check_launch("graft_update_adjacency_tree");
   if (st != GRAFT_OK) return st;
   const size_t head = tree_pairs_bytes(batch, n_max);
-  // nearly every row is a valid transition here: past 1024 of them the
-  // hash-table path is faster than sorting them in every workgroup
+  // nearly every row is a valid transition here; the per-step path, whose
+  // workgroups each sort only the transitions of their own rows, stays
+  // ahead of the hash-table path up to its capacity (measured at 1040 and
+  // 2080 transitions)
   return update_impl(m_ids, m_scores, vocab, top_s, batch * n_max, 2, pairs, lens, ws + head,
-                     workspace_bytes - head, stream, 1024);
+                     workspace_bytes - head, stream);
 }
 
 // ---------------------------------------------------------------- KV append

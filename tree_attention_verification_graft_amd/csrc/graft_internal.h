@@ -131,9 +131,10 @@ struct UpdateParams {
   char *ws;
   UpdateLayout lay;
 };
-// small_limit: the most potential transitions the single-pass LDS path
-// takes (every workgroup of that path sorts all valid transitions).
-void launch_update(const UpdateParams &p, hipStream_t stream, int32_t small_limit = 4096);
+// Calls of at most 4096 potential transitions take the single-pass LDS path
+// (each workgroup gathers and sorts the transitions of its own rows), larger
+// ones the hash-table path.
+void launch_update(const UpdateParams &p, hipStream_t stream);
 void launch_tree_pairs(int32_t batch, int32_t n_max, const int32_t *tree_token,
                        const int32_t *argmax, const int32_t *n_nodes, int32_t *pairs,
                        int32_t *lens, hipStream_t stream);
