@@ -285,8 +285,8 @@ __device__ void merge_row(int32_t *ids, float *sc, int S, int n, const Get &get,
     return;
   }
 
-  // Many new entries (prompt evidence on a frequent token): S rounds of
-  // "best candidate strictly below the previous pick".
+  // Many new entries (a frequent token): S rounds of "best candidate
+  // strictly below the previous pick".
   if (lane < S) {
     w.sc[lane] = my_sc;
     w.add[lane] = 0u;
@@ -294,6 +294,65 @@ __device__ void merge_row(int32_t *ids, float *sc, int S, int n, const Get &get,
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kRegEntries = 16;  // new entries per lane held in registers
+  if (n <= 64 * kRegEntries) {
+    // Each lane reads its entries once: a resident successor's count goes
+    // to w.add (first entries carry distinct tokens, so no two lanes write
+    // one slot), any other successor becomes a candidate key kept in
+    // registers, and the rounds scan only those.
+    unsigned long long ck[kRegEntries];
+#pragma unroll
+    for (int t = 0; t < kRegEntries; ++t) {
+      ck[t] = 0ull;
+      const int e = lane + 64 * t;
+      if (e < n) {
+        const NewEntry x = get(e);
+        if (x.first) {
+          bool resident = false;
+          for (int q = 0; q < S; ++q) {
+            if (w.id[q] == x.v) {
+              w.add[q] = x.count;
+              resident = true;
+            }
+          }
+          if (!resident) ck[t] = cand_key((float)x.count, x.v);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    unsigned long long last = ~0ull;
+    for (int r = 0; r < S; ++r) {
+      unsigned long long best = 0ull;
+      if (lane < S && w.id[lane] >= 0) {
+        const unsigned long long k = cand_key(w.sc[lane] + (float)w.add[lane], w.id[lane]);
+        if (k < last) best = k;
+      }
+#pragma unroll
+      for (int t = 0; t < kRegEntries; ++t)
+        if (ck[t] < last && ck[t] > best) best = ck[t];
+      for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long y = __shfl_xor(best, o);
+        best = y > best ? y : best;
+      }
+      // the old row lives in LDS, so writing slot r cannot disturb the reads
+      if (lane == 0) {
+        ids[r] = best ? key_id(best) : -1;
+        sc[r] = best ? key_score(best) : 0.f;
+      }
+      if (best == 0ull) {
+        for (int q = r + 1 + lane; q < S; q += 64) {
+          ids[q] = -1;
+          sc[q] = 0.f;
+        }
+        break;
+      }
+      last = best;
+    }
+    return;
+  }
+  // Longer rows read their entries again in every round.
   for (int e = lane; e < n; e += 64) {
     const NewEntry x = get(e);
     if (!x.first) continue;
