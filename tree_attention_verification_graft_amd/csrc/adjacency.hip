@@ -212,51 +212,12 @@ __device__ inline float key_score(unsigned long long k) {
 __device__ inline int key_id(unsigned long long k) { return (int)(~(uint32_t)(k & 0xffffffffull)); }
 
 // Per-wave LDS scratch of the row merge.
-// Lane l's key and the key of lane l ^ stride (stride < 64), as an
-// unordered pair {a, b}, which is all a compare-exchange needs.  Strides up
-// to 8 move the partner's halves with DPP lane permutes within rows of 16
-// (xor 1 and 2 are quad permutes; xor 4 is the half-row mirror then the
-// quad reversal, xor 8 the row mirror then the half-row mirror); 16 and 32
-// use the gfx950 row-swap permutes, whose two results hold the lane's own
-// value and its partner's.  All 64 lanes must be active.
-__device__ inline uint32_t dpp_xor(uint32_t v, int stride) {
-  constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadRev = 0x1B;
-  constexpr int kHalfMirror = 0x141, kMirror = 0x140;
-  const int x = (int)v;
-  switch (stride) {
-    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(x, x, kQuadXor1, 0xF, 0xF, false);
-    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(x, x, kQuadXor2, 0xF, 0xF, false);
-    case 4: {
-      const int t = __builtin_amdgcn_update_dpp(x, x, kHalfMirror, 0xF, 0xF, false);
-      return (uint32_t)__builtin_amdgcn_update_dpp(t, t, kQuadRev, 0xF, 0xF, false);
-    }
-    default: {  // 8
-      const int t = __builtin_amdgcn_update_dpp(x, x, kMirror, 0xF, 0xF, false);
-      return (uint32_t)__builtin_amdgcn_update_dpp(t, t, kHalfMirror, 0xF, 0xF, false);
-    }
-  }
-}
-__device__ inline void xor_pair(unsigned long long x, int stride, unsigned long long &a,
-                                unsigned long long &b) {
-  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-  if (stride <= 8) {
-    a = x;
-    b = ((unsigned long long)dpp_xor(hi, stride) << 32) | dpp_xor(lo, stride);
-  } else {
-    const auto l = stride == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
-                                : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    const auto h = stride == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
-                                : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    a = ((unsigned long long)h[0] << 32) | l[0];
-    b = ((unsigned long long)h[1] << 32) | l[1];
-  }
-}
 // One bitonic step at position i of lane-held keys, partner i ^ stride in
 // the same wave: the lower position keeps the min when the block sorts up.
 __device__ inline unsigned long long bitonic_step(unsigned long long x, int i, int size,
                                                   int stride) {
   unsigned long long a, b;
-  xor_pair(x, stride, a, b);
+  lane_pair(x, stride, a, b);
   const unsigned long long mn = a < b ? a : b, mx = a < b ? b : a;
   const bool up = (i & size) == 0, lower = (i & stride) == 0;
   return lower == up ? mn : mx;
@@ -385,7 +346,7 @@ __device__ void merge_row(int32_t *ids, float *sc, int S, int n, const Get &get,
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
         unsigned long long a, b;
-        xor_pair(best, o, a, b);
+        lane_pair(best, o, a, b);
         best = a > b ? a : b;
       }
       // the old row lives in LDS, so writing slot r cannot disturb the reads
@@ -433,7 +394,7 @@ __device__ void merge_row(int32_t *ids, float *sc, int S, int n, const Get &get,
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       unsigned long long a, b;
-      xor_pair(best, o, a, b);
+      lane_pair(best, o, a, b);
       best = a > b ? a : b;
     }
     // the old row lives in LDS, so writing slot r cannot disturb the reads

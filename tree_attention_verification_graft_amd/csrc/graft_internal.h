@@ -10,6 +10,53 @@
 
 namespace graft {
 
+// ---- wave-wide exchanges that stay in the vector ALU.  lane_pair gives
+// lane l's value and the value of lane l ^ stride (stride 1, 2, 4, ..., 32)
+// as an unordered pair {a, b}, which is all a maximum, a sum or a
+// compare-exchange needs.  Strides up to 8 move the partner's value with DPP
+// lane permutes within rows of 16 (xor 1 and 2 are quad permutes; xor 4 is
+// the half-row mirror then the quad reversal, xor 8 the row mirror then the
+// half-row mirror); 16 and 32 use the gfx950 row-swap permutes, whose two
+// results hold the lane's own value and its partner's.  All 64 lanes must be
+// active.
+__device__ inline uint32_t dpp_lane_xor(uint32_t v, int stride) {
+  constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadRev = 0x1B;
+  constexpr int kHalfMirror = 0x141, kMirror = 0x140;
+  const int x = (int)v;
+  switch (stride) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(x, x, kQuadXor1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(x, x, kQuadXor2, 0xF, 0xF, false);
+    case 4: {
+      const int t = __builtin_amdgcn_update_dpp(x, x, kHalfMirror, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_update_dpp(t, t, kQuadRev, 0xF, 0xF, false);
+    }
+    default: {  // 8
+      const int t = __builtin_amdgcn_update_dpp(x, x, kMirror, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_update_dpp(t, t, kHalfMirror, 0xF, 0xF, false);
+    }
+  }
+}
+__device__ inline void lane_pair(uint32_t v, int stride, uint32_t &a, uint32_t &b) {
+  if (stride <= 8) {
+    a = v;
+    b = dpp_lane_xor(v, stride);
+  } else {
+    const auto r = stride == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                                : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+}
+__device__ inline void lane_pair(unsigned long long v, int stride, unsigned long long &a,
+                                 unsigned long long &b) {
+  uint32_t al, bl, ah, bh;
+  lane_pair((uint32_t)v, stride, al, bl);
+  lane_pair((uint32_t)(v >> 32), stride, ah, bh);
+  a = ((unsigned long long)ah << 32) | al;
+  b = ((unsigned long long)bh << 32) | bl;
+}
+
+
 // Thread-local error message behind graft_last_error().
 graft_status set_error(graft_status code, const char *fmt, ...);
 
