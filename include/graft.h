@@ -353,9 +353,14 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max,
  * when rand_sample * (residual mass) lies within about 1e-13 (relative) of
  * a token's cumulative boundary.
  * workspace: >= graft_accept_sample_workspace_size(...) bytes, any contents
- * (per-chunk row statistics, per-chunk residual masses of the stop row and
- * a per-sequence record between the launches).  Calls that share one
- * workspace must not overlap.
+ * (chunk statistics, the stop row's residual mass per chunk and a
+ * per-sequence record between the launches).  Calls that share one
+ * workspace must not overlap.  Trees of at most 384 MiB of logits (and at
+ * most 2304 vocabulary chunks of 4096 bf16 or 2048 f32 entries) read every
+ * row once, at a cost independent of how deep the walks go; larger ones
+ * read the root row and then only the rows a walk reaches, one workgroup
+ * per sequence, at a cost that grows with the deepest walk of the batch.
+ * Any vocabulary size is accepted.
  */
 size_t graft_accept_sample_workspace_size(graft_dtype dtype, int32_t batch, int32_t n_max,
                                           int32_t vocab);

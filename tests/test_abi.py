@@ -177,13 +177,26 @@ def test_accept_sample_validation():
     assert acc(ws=None) == -3
     assert acc(b=0) == 0
     align = lambda x: -(-x // 256) * 256
-    # a 16-byte (float max, float64 sum) record per (row, vocab chunk of
-    # 4096 bf16 or 2048 f32 entries), a float64 mass per (sequence, chunk)
-    # of the stop row, and a 544-byte hand-over record per sequence
-    for dt, ch in ((1, 38), (0, 75)):
-        want = align(2 * 65 * ch * 16) + align(2 * ch * 8) + align(2 * 544)
-        assert lib.graft_accept_sample_workspace_size(dt, 2, 65, 151936) == want
-    assert acc(v=2304 * 4096 + 1) == -2   # more chunks than one workgroup stages
+    # staged mode while the tree's logits take at most 384 MiB and a row has
+    # at most 2304 chunks of 4096 bf16 or 2048 f32 entries: a 16-byte (float
+    # max, float64 sum) record per (row, chunk); else lazy mode: a 32-byte
+    # record per (sequence, chunk) of the root row.  Then a float64 residual
+    # mass per (sequence, chunk) and a 544-byte record per sequence.
+    def want(dt, B, n, V):
+        e, per = (2, 4096) if dt == 1 else (4, 2048)
+        ch = -(-V // per)
+        lazy = B * n * V * e > 384 << 20 or ch > 2304
+        recs = B * ch * 32 if lazy else B * n * ch * 16
+        return align(recs) + align(B * ch * 8) + align(B * 544)
+    for dt in (1, 0):
+        for B, n, V in ((2, 65, 151936), (16, 65, 151936), (32, 65, 151936), (1, 1, 151936),
+                        (2, 3, 2304 * 4096), (2, 3, 2304 * 4096 + 1), (1, 2, 1)):
+            assert lib.graft_accept_sample_workspace_size(dt, B, n, V) == want(dt, B, n, V)
+    # staged at (8, 65, 151936) bf16, lazy at (32, 65, 151936) and past 2304 chunks
+    assert want(1, 8, 65, 151936) == align(8 * 65 * 38 * 16) + align(8 * 38 * 8) + align(8 * 544)
+    assert want(1, 32, 65, 151936) == align(32 * 38 * 32) + align(32 * 38 * 8) + align(32 * 544)
+    assert want(1, 2, 3, 2304 * 4096 + 1) == (align(2 * 2305 * 32) + align(2 * 2305 * 8)
+                                              + align(2 * 544))
     assert lib.graft_accept_sample_workspace_size(5, 2, 65, 151936) == 0
 
 

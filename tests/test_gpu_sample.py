@@ -175,37 +175,67 @@ def _random_case(seed, B, n_max, V, dtype, boost, repeat_frac=0.3):
     return logits, token, parent, n_nodes
 
 
+# A tree whose logits take at most 384 MiB (and whose rows' chunk records
+# fit the staging area) is sampled in staged mode: statistics of every row,
+# then one walk per workgroup.  A larger one, or a vocabulary past 2304
+# chunks, takes lazy mode: the root's records, the walk reading each deeper
+# row it reaches, and the residual and pick launches after a stop below the
+# root.  (dtype, batch, n_max, vocab, temperature)
 RANDOM = [
-    ("bf16", 9, 1000, 1.0), ("bf16", 65, 4103, 0.8), ("bf16", 128, 20000, 1.3),
-    ("f32", 9, 999, 1.0), ("f32", 65, 4096, 0.5), ("f32", 128, 9001, 2.5),
-    ("bf16", 33, 70001, 0.05), ("f32", 17, 3000, 0.05),
-    # more than 8192 (row, chunk) pairs: statistics chunks of eight loads per
-    # thread (16384 bf16 / 8192 f32 entries), the last one ragged
-    ("bf16", 128, 30000, 1.0), ("f32", 128, 12001, 0.9),
+    # staged
+    ("bf16", 12, 9, 1000, 1.0), ("bf16", 12, 65, 4103, 0.8), ("bf16", 12, 128, 20000, 1.3),
+    ("f32", 12, 9, 999, 1.0), ("f32", 12, 65, 4096, 0.5), ("f32", 12, 128, 9001, 2.5),
+    ("bf16", 12, 33, 70001, 0.05), ("f32", 12, 17, 3000, 0.05),
+    # ... more than 8192 (row, chunk) pairs: statistics chunks of eight loads
+    # per thread (16384 bf16 / 8192 f32 entries), the last one ragged
+    ("bf16", 12, 128, 30000, 1.0), ("f32", 12, 128, 12001, 0.9),
+    # lazy: rows ragged in the last chunk
+    ("bf16", 96, 33, 70001, 1.0), ("f32", 72, 128, 12001, 0.9),
+    # ... rows longer than one round of the walk's row pass (131072 bf16 /
+    # 65536 f32 entries per round of sixteen 16-byte loads per thread), so
+    # that a thread's running sum is rescaled when a later round raises its
+    # max; the third takes the entry-at-a-time path over several rounds
+    ("bf16", 28, 48, 151936, 0.7), ("f32", 48, 16, 140000, 1.0), ("bf16", 64, 24, 140001, 1.0),
+    # ... deep walks at a low temperature
+    ("bf16", 48, 65, 70001, 0.05),
+    # ... and a vocabulary of more than 2304 chunks of 4096
+    ("bf16", 2, 3, 2304 * 4096 + 1, 1.0),
 ]
 
 
-@pytest.mark.parametrize("dtype,n_max,V,T", RANDOM,
-                         ids=[f"{d}-n{n}-V{v}-T{t}" for d, n, v, t in RANDOM])
-def test_random_trees(dtype, n_max, V, T):
-    B = 12
+def _lazy(dtype, B, n_max, V):
+    e, per_chunk = (2, 4096) if dtype == "bf16" else (4, 2048)
+    return B * n_max * V * e > 384 << 20 or -(-V // per_chunk) > 2304
+
+
+@pytest.mark.parametrize("dtype,B,n_max,V,T", RANDOM,
+                         ids=[f"{d}-B{b}-n{n}-V{v}-T{t}" for d, b, n, v, t in RANDOM])
+def test_random_trees(dtype, B, n_max, V, T):
     amb = 0
-    for rep in range(2):
+    lazy = _lazy(dtype, B, n_max, V)
+    for rep in range(1 if lazy else 2):
         logits, token, parent, n_nodes = _random_case(1000 * n_max + V + rep, B, n_max, V,
                                                       dtype, boost=6.0)
         ra, rs = W.sampling_uniforms(7 + rep, B, n_max)
         got = run_sample(logits, dtype, T, token, parent, n_nodes, ra, rs)
         ref = oracle_sample(logits, dtype, T, token, parent, n_nodes, ra, rs)
         amb += compare(ref, got, parent, token, n_nodes, V)
-    _say(f"[sample] random {dtype} n_max={n_max} V={V} T={T}: ok, ambiguous {amb}")
+    _say(f"[sample] random {dtype} B={B} n_max={n_max} V={V} T={T} "
+         f"{'lazy' if lazy else 'staged'}: ok, ambiguous {amb}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_rejected_mass_leaves_an_exact_residual(dtype):
+# staged, and lazy by a vocabulary of more than 2304 chunks (then the root
+# kernel's residual sums leave the rejected tokens out)
+RESIDUAL = [("bf16", 8, 12, 30000), ("f32", 8, 12, 30000),
+            ("bf16", 1, 12, 2304 * 4096 + 1), ("f32", 1, 12, 2304 * 2048 + 1)]
+
+
+@pytest.mark.parametrize("dtype,B,n_max,V", RESIDUAL,
+                         ids=[f"{d}-B{b}-V{v}" for d, b, n, v in RESIDUAL])
+def test_rejected_mass_leaves_an_exact_residual(dtype, B, n_max, V):
     """The root's children carry almost all the mass and every one is
     rejected: the bonus is drawn from the small residual, whose chunks that
     held the rejected tokens are summed exactly."""
-    B, n_max, V = 8, 12, 30000
     rng = np.random.default_rng(5)
     parent = np.zeros((B, n_max), np.int32)
     parent[:, 0] = -1
@@ -228,9 +258,10 @@ def test_rejected_mass_leaves_an_exact_residual(dtype):
         assert int(got[2][b, 1]) not in set(token[b, 1:].tolist())
 
 
-def test_root_only_and_deterministic():
+@pytest.mark.parametrize("B,V", [(6, 4099), (2, 2304 * 4096 + 1)], ids=["staged", "lazy"])
+def test_root_only_and_deterministic(B, V):
     """Root-only trees sample the bonus by inverse CDF; two calls agree."""
-    B, n_max, V = 6, 5, 4099
+    n_max = 5
     logits, token, parent, _ = _random_case(77, B, n_max, V, "bf16", boost=3.0)
     n_nodes = np.ones(B, np.int32)
     ra, rs = W.sampling_uniforms(3, B, n_max)

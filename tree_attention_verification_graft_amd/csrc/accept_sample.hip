@@ -10,24 +10,43 @@
 // token ids.  The random numbers are inputs (one per child for its test, one
 // per node for its bonus draw).
 //
-// Three launches:
-//  * row_stats_kernel, one workgroup per (node row, vocabulary chunk of two
-//    or eight 16-byte loads per thread): the chunk's max m and its sum of
-//    2^((l - m) log2(e) / T), one float32 exponential per entry, summed
-//    pairwise in float32 within a load and in float64 across loads; the
-//    sum's relative error stays near 1e-6 (the product's rounding in the
-//    exponent dominates), a few ALU operations per entry so that the pass
-//    streams the logits at close to the rate of the greedy argmax.
-//  * sample_walk_kernel, one workgroup per (vocabulary chunk, sequence):
+// Two modes, by the size of the tree's logits.
+//
+// Staged mode (at most 384 MiB of logits), three launches whose cost does
+// not depend on how deep the walks go:
+//  * chunk_stats_kernel, one workgroup per (node row, vocabulary chunk):
+//    every row's chunk max and float32-exponential sum.
+//  * sample_staged_kernel, one workgroup per (vocabulary chunk, sequence):
 //    every workgroup of a sequence stages the chunk statistics of all node
 //    rows in LDS, folds them to per-row (max, sum), computes each node's
-//    proposal probability p_parent(token) and walks the tree on one wave
-//    (all of them identically).  Then each workgroup sums the float64
-//    masses of its own chunk of the stop node's row, rejected tokens left
-//    out; the first workgroup writes the accepted path.
-//  * sample_pick_kernel, one workgroup per sequence: a block scan over the
-//    chunk masses finds the chunk that holds rand_sample * total, a block
-//    scan over that chunk's float64 masses finds the token.
+//    proposal probability and walks the tree on one wave (all of them
+//    identically).  Then each sums the float64 masses of its own chunk of
+//    the stop node's row, rejected tokens left out.
+//  * sample_pick_kernel, one workgroup per sequence, the bonus draw.
+//
+// Lazy mode (larger trees, or vocabularies whose chunk records exceed the
+// staging area) reads only the rows a walk reaches:
+//  * sample_root_kernel, one workgroup per (vocabulary chunk, sequence):
+//    the root row's chunk max and float64 mass sums over all entries and
+//    over those that are not a root child's token.
+//  * sample_walk_kernel, one workgroup of 1024 threads per sequence: from
+//    the root, the current node's row statistics (max m and sum of
+//    2^((l - m) log2(e) / T)), then its children tried in index order on
+//    one wave.  At the root the statistics fold the root's records; below
+//    it the workgroup reads the row once, one float32 exponential per
+//    entry, summed pairwise in float32 within a 16-byte load and in float64
+//    across loads (relative error near 1e-6).  A stop at the root rejected
+//    every root child, whose tokens the records' residual sums already
+//    leave out, so the walk draws the bonus token itself; a stop below it
+//    is handed on, with its row max and rejected tokens, to
+//  * sample_residual_kernel, one workgroup per (vocabulary chunk,
+//    sequence): the float64 masses of its chunk of the stop node's row,
+//    rejected tokens left out, and
+//  * sample_pick_kernel, the bonus draw.
+//
+// The bonus draw: a block scan over the chunk masses finds the chunk that
+// holds rand_sample * total, a block scan over that chunk's float64 masses
+// finds the token.
 //
 // The bonus token is located among intervals of width p(y), often below
 // 1e-5 of the total for large vocabularies, so its masses are float64 end
@@ -50,6 +69,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLoads = 2;  // 16-byte loads per thread per chunk
 constexpr int kStageLoads = kSampleStage / kThreads;
+constexpr int kWalkThreads = 1024;  // the lazy walk's workgroup
+constexpr int kWalkWaves = kWalkThreads / 64;
+constexpr int kRowLoads = 16;  // 16-byte loads per thread per round of a lazy row pass
 template <bool BF16>
 constexpr int per_load() { return BF16 ? 8 : 4; }
 template <bool BF16>
@@ -231,6 +253,7 @@ __device__ inline double block_sum_d(double x, double *red) {
 // is bit-identical to thread t-1's inclusive one and the last thread's
 // inclusive prefix to the total, so the intervals [excl, incl) tile
 // [0, total) without gaps or overlaps.
+template <int W = kWaves>
 __device__ inline double block_scan_d(double x, double *red, double *excl, double *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int o = 1; o < 64; o <<= 1) {
@@ -243,7 +266,7 @@ __device__ inline double block_scan_d(double x, double *red, double *excl, doubl
   __syncthreads();
   double before = 0.0, t = 0.0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     if (w < wave) before += red[w];
     t += red[w];
   }
@@ -271,9 +294,148 @@ __device__ inline float exp2_split(float d, float k_hi, float k_lo) {
   return xh > -160.f ? r : 0.f;
 }
 
+// ------------------------------------------------------------ the bonus draw
+struct PickShared {
+  double red[kWalkWaves];
+  double tin;
+  int cstar, clast, bonus, elast;
+};
+
+// The bonus token of sequence b, drawn from the residual of stop node s:
+// a block scan over the chunk masses chunk_w[b][*] (w0: thread t's mass of
+// chunk t) finds the chunk that holds u * total, a block scan over that
+// chunk's float64 masses finds the token, written after the len path
+// tokens.  NT threads take part; the first kThreads hold the chunk's
+// entries.
+template <bool BF16, bool VEC, int NT>
+__device__ void bonus_pick(const SampleParams &p, int b, int s, int len, float row_max, float u,
+                           const int32_t *s_gone, int ng, double w0, PickShared &sh) {
+  constexpr int W = NT / 64;
+  constexpr int kVals = vals<BF16>();
+  constexpr int kChunk = chunk_len<BF16>();
+  const int tid = threadIdx.x;
+  const int chunks = p.wchunks;
+  const double *w_row = p.chunk_w + (size_t)b * chunks;
+  if (tid == 0) {
+    sh.cstar = -1;
+    sh.clast = -1;
+    sh.bonus = -1;
+    sh.elast = -1;
+  }
+  // total residual mass, then the chunk holding the target.  With at most
+  // one chunk per thread a single scan gives both; otherwise the same scan
+  // runs twice, so that the final carry equals the total bit for bit.  (The
+  // scans' barriers order the initialisation above before its uses.)
+  double total = 0.0, incl0 = 0.0, ex0 = 0.0;
+  for (int c0 = 0; c0 < chunks; c0 += NT) {
+    const int c = c0 + tid;
+    const double w = c0 == 0 ? w0 : (c < chunks ? w_row[c] : 0.0);
+    double ex, gt;
+    const double incl = block_scan_d<W>(w, sh.red, &ex, &gt);
+    if (c0 == 0) {
+      incl0 = incl;
+      ex0 = ex;
+    }
+    total += gt;
+  }
+  const double target = (double)u * total;
+  double carry = 0.0;
+  for (int c0 = 0; c0 < chunks; c0 += NT) {
+    const int c = c0 + tid;
+    const double w = c0 == 0 ? w0 : (c < chunks ? w_row[c] : 0.0);
+    double ex = ex0, incl = incl0, gt = total;
+    if (chunks > NT) incl = block_scan_d<W>(w, sh.red, &ex, &gt);
+    const double lo = carry + ex, hi = carry + incl;
+    if (w > 0.0) {
+      atomicMax(&sh.clast, c);
+      if (target >= lo && target < hi) {
+        sh.cstar = c;
+        sh.tin = target - lo;
+      }
+    }
+    carry += gt;
+  }
+  __syncthreads();
+  int cstar = sh.cstar;
+  double tin = sh.tin;
+  if (cstar < 0) {
+    // total 0 (every token rejected), or rounding put the target at the top
+    cstar = sh.clast;
+    tin = cstar >= 0 ? w_row[cstar] : 0.0;
+  }
+  if (cstar >= 0) {
+    // the chunk's float64 masses, each of the first kThreads threads a
+    // contiguous run of entries (the loads of the others fall past the
+    // chunk and read as -inf)
+    const size_t srow = (size_t)b * p.n_max + s;
+    const int lo_e = cstar * kChunk;
+    float v[kVals];
+    load_chunk_contig<BF16, VEC>(p.logits, srow, p.vocab, lo_e, v);
+    const uint32_t bits = gone_bits_contig<BF16>(s_gone, ng, lo_e);
+    // a row of -inf logits has no mass: compare against -inf as a max of 0
+    const float mref = row_max > -INFINITY ? row_max : 0.f;
+    double mass[kVals];
+    double gs = 0.0;
+    int jlast = -1;
+#pragma unroll
+    for (int k = 0; k < kVals; ++k)
+      mass[k] = mass64(v[k], mref, p.k_log2) * (double)(1u - ((bits >> k) & 1u));
+#pragma unroll
+    for (int k = 0; k < kVals; ++k) {
+      gs += mass[k];
+      if (mass[k] > 0.0) jlast = k;
+    }
+    const int e0 = lo_e + tid * kVals;
+    if (jlast >= 0) atomicMax(&sh.elast, e0 + jlast);
+    double ex, gt;
+    const double incl = block_scan_d<W>(gs, sh.red, &ex, &gt);
+    if (gs > 0.0 && tin >= ex && tin < incl) {
+      double acc = ex;
+      int pick = jlast;
+#pragma unroll
+      for (int k = 0; k < kVals; ++k) {
+        acc += mass[k];
+        if (acc > tin && mass[k] > 0.0) {
+          pick = k;
+          break;
+        }
+      }
+      sh.bonus = e0 + pick;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int y = sh.bonus;
+    if (y < 0) y = sh.elast >= 0 ? sh.elast : p.vocab - 1;
+    p.path_tokens[(size_t)b * (p.n_max + 1) + len] = y;
+  }
+}
+
+// One workgroup per sequence: the bonus draw from the chunk masses of the
+// staged walk, or of the residual launch after a lazy walk that stopped
+// below the root.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleParams p) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ int32_t s_gone[GRAFT_MAX_NODES];
+  __shared__ PickShared sh;
+  const SampleRec *rec = p.rec + b;
+  const int s = rec->stop;
+  if (p.lazy && s == 0) return;  // the lazy walk drew it
+  const int len = rec->len, ng = rec->ngone;
+  const double w0 = tid < p.wchunks ? p.chunk_w[(size_t)b * p.wchunks + tid] : 0.0;
+  if (tid < ng) s_gone[tid] = rec->gone[tid];
+  bonus_pick<BF16, VEC, kThreads>(p, b, s, len, rec->row_max, rec->u, s_gone, ng, w0, sh);
+}
+
+// ===================================================== staged mode (small trees)
 // ------------------------------------------------------------ row statistics
+// One workgroup per (vocabulary chunk, node row): the chunk's max and its
+// sum of float32 2^((l - m) log2(e) / T), summed pairwise in float32 within
+// a load and in float64 across loads.
 template <bool BF16, bool VEC, int L>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(SampleParams p) {
+__global__ __launch_bounds__(kThreads) void chunk_stats_kernel(SampleParams p) {
   constexpr int kPer = per_load<BF16>();
   constexpr int kV = L * kPer;
   const int c = blockIdx.x;
@@ -317,9 +479,16 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(SampleParams p) {
   }
 }
 
-// ------------------------------------------------------------------ the walk
+// ------------------------------------------------------- the staged walk
+// One workgroup per (vocabulary chunk, sequence).  Every workgroup of a
+// sequence stages the chunk statistics of all node rows in LDS, folds them
+// to per-row (max, sum), computes each node's proposal probability
+// p_parent(token) and walks the tree on one wave (all of them
+// identically).  Then each sums the float64 masses of its own chunk of the
+// stop node's row, rejected tokens left out; the first writes the accepted
+// path and the hand-over record of the pick launch.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_walk_kernel(SampleParams p) {
+__global__ __launch_bounds__(kThreads) void sample_staged_kernel(SampleParams p) {
   constexpr int kVals = vals<BF16>();
   constexpr int kChunk = chunk_len<BF16>();
   const int c_own = blockIdx.x;  // this workgroup's chunk of the stop row
@@ -496,122 +665,414 @@ __global__ __launch_bounds__(kThreads) void sample_walk_kernel(SampleParams p) {
   }
 }
 
-// ------------------------------------------------------------ the bonus draw
+// ====================================================== lazy mode (large trees)
+// Lane l's double (l wave-uniform).
+__device__ inline double readlane_d(double v, int l) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+template <int W>
+__device__ inline float block_max_f(float x, float *red) {
+  x = wave_max_f(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) t = fmaxf(t, red[w]);
+  __syncthreads();
+  return t;
+}
+template <int W>
+__device__ inline double block_sum_w(double x, double *red) {
+  x = wave_sum_d(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// ------------------------------------------------------------ the root row
+// One workgroup per (vocabulary chunk, sequence): the chunk's max and
+// float64 mass sums of the root's row relative to that max, over all
+// entries (for the root's acceptance tests) and over the entries that are
+// not a token of the root's children.  A walk that stops at the root has
+// tried and rejected every child, so the second sum is its residual mass
+// there, and no later launch reads the root row in full again.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleParams p) {
+__global__ __launch_bounds__(kThreads) void sample_root_kernel(SampleParams p) {
   constexpr int kVals = vals<BF16>();
   constexpr int kChunk = chunk_len<BF16>();
-  const int b = blockIdx.x;
+  constexpr int node = 0;
+  const int c_own = blockIdx.x;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   __shared__ int32_t s_gone[GRAFT_MAX_NODES];
-  __shared__ double s_red[kWaves];
-  __shared__ int s_cstar, s_clast, s_bonus, s_elast;
-  __shared__ double s_tin;
-
-  const SampleRec *rec = p.rec + b;
-  const int chunks = p.wchunks;
-  const double *w_row = p.chunk_w + (size_t)b * chunks;
-  // one round: the record and the first group of chunk masses
-  const int s = rec->stop, len = rec->len, ng = rec->ngone;
-  const float row_max = rec->row_max;
-  const float u = rec->u;
-  const double w0 = tid < chunks ? w_row[tid] : 0.0;
-  if (tid < ng) s_gone[tid] = rec->gone[tid];
-  if (tid == 0) {
-    s_cstar = -1;
-    s_clast = -1;
-    s_bonus = -1;
-    s_elast = -1;
-  }
-  // total residual mass, then the chunk holding the target.  With at most
-  // one chunk per thread a single scan gives both; otherwise the same scan
-  // runs twice, so that the final carry equals the total bit for bit.
-  double total = 0.0, incl0 = 0.0, ex0 = 0.0;
-  for (int c0 = 0; c0 < chunks; c0 += kThreads) {
-    const int c = c0 + tid;
-    const double w = c0 == 0 ? w0 : (c < chunks ? w_row[c] : 0.0);
-    double ex, gt;
-    const double incl = block_scan_d(w, s_red, &ex, &gt);
-    if (c0 == 0) {
-      incl0 = incl;
-      ex0 = ex;
-    }
-    total += gt;
-  }
-  const double target = (double)u * total;
-  double carry = 0.0;
-  for (int c0 = 0; c0 < chunks; c0 += kThreads) {
-    const int c = c0 + tid;
-    const double w = c0 == 0 ? w0 : (c < chunks ? w_row[c] : 0.0);
-    double ex = ex0, incl = incl0, gt = total;
-    if (chunks > kThreads) incl = block_scan_d(w, s_red, &ex, &gt);
-    const double lo = carry + ex, hi = carry + incl;
-    if (w > 0.0) {
-      atomicMax(&s_clast, c);
-      if (target >= lo && target < hi) {
-        s_cstar = c;
-        s_tin = target - lo;
-      }
-    }
-    carry += gt;
-  }
+  __shared__ int s_ng;
+  __shared__ float s_redf[kWaves];
+  __shared__ double s_redz[kWaves], s_redr[kWaves];
+  const size_t base_row = (size_t)b * p.n_max;
+  const int n = min(max(p.n_nodes[b], 1), p.n_max);
+  // the root's children: later nodes whose parent it is
+  int tok = 0;
+  const bool child = tid > node && tid < n && p.tree_parent[base_row + tid] == node;
+  if (child) tok = p.tree_token[base_row + tid];
+  float v[kVals];
+  load_chunk_contig<BF16, VEC>(p.logits, base_row + node, p.vocab, c_own * kChunk, v);
+  if (tid == 0) s_ng = 0;
   __syncthreads();
-  int cstar = s_cstar;
-  double tin = s_tin;
-  if (cstar < 0) {
-    // total 0 (every token rejected), or rounding put the target at the top
-    cstar = s_clast;
-    tin = cstar >= 0 ? w_row[cstar] : 0.0;
+  if (child) s_gone[atomicAdd(&s_ng, 1)] = tok;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kVals; ++k) mt = fmaxf(mt, v[k]);
+  const float mc = block_max_f<kWaves>(mt, s_redf);  // its barriers publish s_gone
+  const uint32_t bits = gone_bits_contig<BF16>(s_gone, s_ng, c_own * kChunk);
+  const float mref = mc > -INFINITY ? mc : 0.f;  // -inf chunk: no mass
+  double zt = 0.0, rt = 0.0;
+#pragma unroll
+  for (int k = 0; k < kVals; ++k) {
+    const double mk = mass64(v[k], mref, p.k_log2);
+    zt += mk;
+    rt += mk * (double)(1u - ((bits >> k) & 1u));
   }
-  if (cstar >= 0) {
-    // the chunk's float64 masses, each thread a contiguous run of entries
-    const size_t srow = (size_t)b * p.n_max + s;
-    const int lo_e = cstar * kChunk;
-    float v[kVals];
-    load_chunk_contig<BF16, VEC>(p.logits, srow, p.vocab, lo_e, v);
-    const uint32_t bits = gone_bits_contig<BF16>(s_gone, ng, lo_e);
-    // a row of -inf logits has no mass: compare against -inf as a max of 0
-    const float mref = row_max > -INFINITY ? row_max : 0.f;
-    double mass[kVals];
-    double gs = 0.0;
-    int jlast = -1;
-#pragma unroll
-    for (int k = 0; k < kVals; ++k)
-      mass[k] = mass64(v[k], mref, p.k_log2) * (double)(1u - ((bits >> k) & 1u));
-#pragma unroll
-    for (int k = 0; k < kVals; ++k) {
-      gs += mass[k];
-      if (mass[k] > 0.0) jlast = k;
-    }
-    const int e0 = lo_e + tid * kVals;
-    if (jlast >= 0) atomicMax(&s_elast, e0 + jlast);
-    double ex, gt;
-    const double incl = block_scan_d(gs, s_red, &ex, &gt);
-    if (gs > 0.0 && tin >= ex && tin < incl) {
-      double acc = ex;
-      int pick = jlast;
-#pragma unroll
-      for (int k = 0; k < kVals; ++k) {
-        acc += mass[k];
-        if (acc > tin && mass[k] > 0.0) {
-          pick = k;
-          break;
-        }
-      }
-      s_bonus = e0 + pick;
-    }
+  zt = wave_sum_d(zt);
+  rt = wave_sum_d(rt);
+  if ((tid & 63) == 0) {
+    s_redz[tid >> 6] = zt;
+    s_redr[tid >> 6] = rt;
   }
   __syncthreads();
   if (tid == 0) {
-    int y = s_bonus;
-    if (y < 0) y = s_elast >= 0 ? s_elast : p.vocab - 1;
-    p.path_tokens[(size_t)b * (p.n_max + 1) + len] = y;
+    double z = 0.0, r = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      z += s_redz[w];
+      r += s_redr[w];
+    }
+    RootChunk out;
+    out.z = z;
+    out.r = r;
+    out.m = mc;
+    out.pad[0] = out.pad[1] = out.pad[2] = 0;
+    p.root[(size_t)b * p.wchunks + c_own] = out;
   }
 }
 
-// 16-byte loads per thread of a statistics chunk: 2 (4096 bf16 / 2048 f32
-// entries) while the grid is small, 8 once it would exceed 8192 workgroups,
-// where fewer and larger workgroups stream faster.
+// ------------------------------------------------------------------ the walk
+
+// The values of one 16-byte load (8 bf16 or 4 float32).
+template <bool BF16>
+__device__ inline void unpack(const uint4 &r, float (&v)[per_load<BF16>()]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (BF16) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    } else {
+      v[q] = __uint_as_float(w[q]);
+    }
+  }
+}
+// Sum of 2^((l - m) k) over one load's values: float32 exponentials summed
+// pairwise in float32.
+template <bool BF16>
+__device__ inline float load_sum(const float (&v)[per_load<BF16>()], float m, float k_hi) {
+  constexpr int kPer = per_load<BF16>();
+  float e[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) e[j] = __builtin_amdgcn_exp2f((v[j] - m) * k_hi);
+#pragma unroll
+  for (int w = kPer / 2; w > 0; w >>= 1)
+#pragma unroll
+    for (int j = 0; j < w; ++j) e[j] += e[j + w];
+  return e[0];
+}
+
+// Statistics of one node row by the whole workgroup: its max m and
+// z = sum of 2^((l - m) log2(e) / T), with one read of the row.  Each thread
+// keeps a running max and a sum relative to it over its rounds of loads:
+// float32 exponentials summed pairwise in float32 within a 16-byte load and
+// in float64 across loads, the sum moved to a new max by a float32 power of
+// two with its product rounding corrected (exp2_split).  The workgroup then
+// folds the threads' sums onto the row max the same way (relative error of
+// z near 1e-6).
+template <bool BF16, bool VEC>
+__device__ void row_stats(const SampleParams &p, size_t row, float *redf, double *redd,
+                          float &m_out, double &z_out) {
+  constexpr int kPer = per_load<BF16>();
+  const int tid = threadIdx.x;
+  const int V = p.vocab;
+  float m = -INFINITY;
+  double z = 0.0;
+  // fold a round's max into the running one, rescaling the sum
+  auto raise = [&](float mr) {
+    if (mr > m) {
+      if (m > -INFINITY) z *= (double)exp2_split(m - mr, p.k_hi, p.k_lo);
+      m = mr;
+    }
+  };
+  if (VEC) {
+    const uint4 *x = reinterpret_cast<const uint4 *>(static_cast<const char *>(p.logits) +
+                                                     row * V * (BF16 ? 2 : 4));
+    const int nvec = V / kPer;
+    for (int r0 = 0; r0 < nvec; r0 += kWalkThreads * kRowLoads) {
+      uint4 raw[kRowLoads];
+#pragma unroll
+      for (int k = 0; k < kRowLoads; ++k) {
+        const int e = r0 + k * kWalkThreads + tid;
+        raw[k] = e < nvec ? x[e] : make_uint4(0u, 0u, 0u, 0u);
+      }
+      float mr = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kRowLoads; ++k) {
+        if (r0 + k * kWalkThreads + tid < nvec) {
+          float v[kPer];
+          unpack<BF16>(raw[k], v);
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) mr = fmaxf(mr, v[j]);
+        }
+      }
+      raise(mr);
+      if (m > -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < kRowLoads; ++k) {
+          if (r0 + k * kWalkThreads + tid < nvec) {
+            float v[kPer];
+            unpack<BF16>(raw[k], v);
+            z += (double)load_sum<BF16>(v, m, p.k_hi);
+          }
+        }
+      }
+    }
+  } else {
+    // rows whose length is not a multiple of the vector width: one entry
+    // at a time, each its own round
+    const size_t base = row * V;
+    for (int e = tid; e < V; e += kWalkThreads) {
+      const float l = logit_at(p.logits, BF16, base + e);
+      raise(l);
+      if (m > -INFINITY) z += (double)__builtin_amdgcn_exp2f((l - m) * p.k_hi);
+    }
+  }
+  const float M = block_max_f<kWalkWaves>(m, redf);
+  const double zt = m > -INFINITY ? z * (double)exp2_split(m - M, p.k_hi, p.k_lo) : 0.0;
+  z_out = block_sum_w<kWalkWaves>(zt, redd);
+  m_out = M;
+}
+
+// One workgroup per sequence walks its tree from the root.  Up front it
+// loads the tree, each node's logit of its own token in its parent's row
+// and the root's chunk records, which wave 0 folds into the root row's max
+// and sum.  At each node it takes the node's row statistics (folded at the
+// root, else one read of the row: only the rows the walk reaches are read)
+// and tries the node's children in index order on wave 0; an accepted
+// child becomes the current node.  At a root stop it also draws the bonus
+// token; below the root it hands the stop node, its row max and rejected
+// tokens to the residual and pick launches.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kWalkThreads) void sample_walk_kernel(SampleParams p) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int32_t s_parent[GRAFT_MAX_NODES];
+  __shared__ int32_t s_token[GRAFT_MAX_NODES];
+  __shared__ float s_u[GRAFT_MAX_NODES];
+  __shared__ float s_lc[GRAFT_MAX_NODES];  // node c's token's logit in its parent's row
+  __shared__ int32_t s_path[GRAFT_MAX_NODES];
+  __shared__ int32_t s_gone[GRAFT_MAX_NODES];  // tokens rejected at the stop node
+  __shared__ float s_redf[kWalkWaves];
+  __shared__ PickShared sh;
+  __shared__ int s_next, s_ngone;
+  __shared__ float s_root_m;
+  __shared__ double s_root_z;
+
+  const size_t base_row = (size_t)b * p.n_max;
+  const int W = p.wchunks;
+  const RootChunk *rc = p.root + (size_t)b * W;
+  // ---- tree arrays and random numbers (one round of loads)
+  const int n = min(max(p.n_nodes[b], 1), p.n_max);
+  if (tid < p.n_max) {
+    int par = p.tree_parent[base_row + tid];
+    int tok = p.tree_token[base_row + tid];
+    if (tid >= n) par = tok = -1;
+    if (par >= tid) par = -1;
+    s_parent[tid] = par;
+    s_token[tid] = tok;
+    s_u[tid] = p.rand_accept[base_row + tid];
+  }
+  __syncthreads();
+  // ---- the candidates' logits and the root's statistics (one round)
+  if (tid < n) {
+    const int par = s_parent[tid], x = s_token[tid];
+    s_lc[tid] = par >= 0 && x >= 0 && x < p.vocab
+                    ? logit_at(p.logits, BF16, (base_row + par) * p.vocab + x)
+                    : -INFINITY;  // no mass: never accepted
+  }
+  if (wave == 0) {
+    // the row max, then the chunk sums moved onto it by float64 powers of two
+    RootChunk r0;
+    r0.m = -INFINITY;
+    r0.z = 0.0;
+    if (lane < W) r0 = rc[lane];
+    float mt = r0.m;
+    for (int c = lane + 64; c < W; c += 64) mt = fmaxf(mt, rc[c].m);
+    const float M = wave_max_f(mt);
+    double zt = r0.m > -INFINITY ? r0.z * mass64(r0.m, M, p.k_log2) : 0.0;
+    for (int c = lane + 64; c < W; c += 64) {
+      const RootChunk rk = rc[c];
+      if (rk.m > -INFINITY) zt += rk.z * mass64(rk.m, M, p.k_log2);
+    }
+    zt = wave_sum_d(zt);
+    if (lane == 0) {
+      s_root_m = M;
+      s_root_z = zt;
+    }
+  }
+  __syncthreads();
+
+  int node = 0, len = 1;
+  float m = -INFINITY;
+  while (true) {
+    double z;
+    if (node == 0) {
+      m = s_root_m;
+      z = s_root_z;
+    } else {
+      row_stats<BF16, VEC>(p, base_row + node, s_redf, sh.red, m, z);
+    }
+    if (wave == 0) {
+      // children of the node in index order: each lane holds the
+      // probability of the child in its slot of a 64-node block
+      double removed = 0.0;
+      int ngone = 0, next = -1;
+      int gone_lo = INT_MIN, gone_hi = INT_MIN;  // lane g holds rejected token g / g + 64
+      for (int base = node + 1; base < n && next < 0; base += 64) {
+        const int c = base + lane;
+        const bool child = c < n && s_parent[c] == node;
+        const double prob = child && z > 0.0 ? mass64(s_lc[c], m, p.k_log2) / z : 0.0;
+        unsigned long long bal = __ballot(child);
+        while (bal) {
+          const int slot = __builtin_ctzll(bal);  // uniform
+          const int cc = base + slot;
+          bal &= bal - 1;
+          const int x = s_token[cc];
+          if (__ballot(gone_lo == x || gone_hi == x)) continue;  // mass already gone
+          const double pc = readlane_d(prob, slot);
+          // u < p(x) / (1 - removed), without the division
+          if ((double)s_u[cc] * (1.0 - removed) < pc) {
+            next = cc;
+            break;
+          }
+          if (ngone < 64) {
+            if (lane == ngone) gone_lo = x;
+          } else if (lane == ngone - 64) {
+            gone_hi = x;
+          }
+          ++ngone;
+          removed += pc;
+        }
+      }
+      if (lane == 0) {
+        s_next = next;
+        s_ngone = ngone;
+      }
+      if (next < 0) {
+        if (lane < ngone) s_gone[lane] = gone_lo;
+        if (lane + 64 < ngone) s_gone[lane + 64] = gone_hi;
+      }
+    }
+    __syncthreads();
+    const int next = s_next;
+    if (next < 0) break;
+    if (tid == 0) s_path[len] = next;
+    node = next;
+    ++len;
+    __syncthreads();  // s_next is read before the next node overwrites it
+  }
+
+  // ---- the accepted path (the bonus token is written by the bonus draw)
+  if (tid == 0) s_path[0] = 0;
+  __syncthreads();
+  const int ng = s_ngone;
+  int32_t *pn = p.path_nodes + base_row;
+  int32_t *pt = p.path_tokens + (size_t)b * (p.n_max + 1);
+  for (int k = tid; k < p.n_max + 1; k += kWalkThreads) {
+    if (k < p.n_max) pn[k] = k < len ? s_path[k] : -1;
+    if (k != len) pt[k] = k < len ? s_token[s_path[k]] : -1;
+  }
+  SampleRec *rec = p.rec + b;
+  const float u = p.rand_sample[base_row + node];
+  if (tid == 0) {
+    p.accept_len[b] = len - 1;
+    rec->stop = node;
+  }
+  if (node == 0) {
+    // every root child was rejected, so the records' residual sums are the
+    // residual's chunk masses, to be moved onto the row max
+    double *cw = p.chunk_w + (size_t)b * W;
+    double w0 = 0.0;
+    for (int c = tid; c < W; c += kWalkThreads) {
+      const RootChunk rk = rc[c];
+      const double w = rk.m > -INFINITY ? rk.r * mass64(rk.m, m, p.k_log2) : 0.0;
+      cw[c] = w;
+      if (c == tid) w0 = w;
+    }
+    __syncthreads();  // chunk_w is read back by other threads
+    bonus_pick<BF16, VEC, kWalkThreads>(p, b, node, len, m, u, s_gone, ng, w0, sh);
+  } else {
+    if (tid < ng) rec->gone[tid] = s_gone[tid];
+    if (tid == 0) {
+      rec->len = len;
+      rec->ngone = ng;
+      rec->row_max = m;
+      rec->u = u;
+    }
+  }
+}
+
+// ------------------------------------------- the stop row's residual masses
+// One workgroup per (vocabulary chunk, sequence): the chunk's float64
+// residual mass of the stop node's row, rejected tokens left out, after a
+// lazy walk that stopped below the root.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_residual_kernel(SampleParams p) {
+  constexpr int kVals = vals<BF16>();
+  constexpr int kChunk = chunk_len<BF16>();
+  const int c_own = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  __shared__ int32_t s_gone[GRAFT_MAX_NODES];
+  __shared__ double s_red[kWaves];
+  const SampleRec *rec = p.rec + b;
+  const int s = rec->stop, ng = rec->ngone;
+  if (s == 0) return;  // the root: the walk drew the bonus token
+  const float row_max = rec->row_max;
+  if (tid < ng) s_gone[tid] = rec->gone[tid];
+  const size_t srow = (size_t)b * p.n_max + s;
+  float v[kVals];
+  load_chunk_contig<BF16, VEC>(p.logits, srow, p.vocab, c_own * kChunk, v);
+  __syncthreads();
+  const uint32_t bits = gone_bits_contig<BF16>(s_gone, ng, c_own * kChunk);
+  const float mref = row_max > -INFINITY ? row_max : 0.f;  // -inf row: no mass
+  double mk[kVals];
+#pragma unroll
+  for (int k = 0; k < kVals; ++k)
+    mk[k] = mass64(v[k], mref, p.k_log2) * (double)(1u - ((bits >> k) & 1u));
+  double part = 0.0;
+#pragma unroll
+  for (int k = 0; k < kVals; ++k) part += mk[k];
+  const double tot = block_sum_d(part, s_red);
+  if (tid == 0) p.chunk_w[(size_t)b * p.wchunks + c_own] = tot;
+}
+
+// 16-byte loads per thread of a staged-mode statistics chunk: 2 (4096 bf16
+// / 2048 f32 entries) while the grid is small, 8 once it would exceed 8192
+// workgroups, where fewer and larger workgroups stream faster.
 constexpr int kStatSmall = 2, kStatLarge = 8, kStatLargeGrid = 8192;
 int stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab) {
   const long long small = (vocab + (long long)kThreads * kStatSmall * (dtype == GRAFT_BF16 ? 8 : 4) - 1) /
@@ -621,16 +1082,30 @@ int stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab) {
 
 template <bool BF16, bool VEC>
 void launch(const SampleParams &p, hipStream_t stream) {
-  if (p.stat_loads == kStatLarge)
-    hipLaunchKernelGGL((row_stats_kernel<BF16, VEC, kStatLarge>), dim3(p.chunks, p.batch * p.n_max),
+  if (!p.lazy) {
+    if (p.stat_loads == kStatLarge)
+      hipLaunchKernelGGL((chunk_stats_kernel<BF16, VEC, kStatLarge>),
+                         dim3(p.chunks, p.batch * p.n_max), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((chunk_stats_kernel<BF16, VEC, kStatSmall>),
+                         dim3(p.chunks, p.batch * p.n_max), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((sample_staged_kernel<BF16, VEC>), dim3(p.wchunks, p.batch),
                        dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((row_stats_kernel<BF16, VEC, kStatSmall>), dim3(p.chunks, p.batch * p.n_max),
-                       dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL((sample_walk_kernel<BF16, VEC>), dim3(p.wchunks, p.batch), dim3(kThreads),
+    hipLaunchKernelGGL((sample_pick_kernel<BF16, VEC>), dim3(p.batch), dim3(kThreads), 0,
+                       stream, p);
+    return;
+  }
+  hipLaunchKernelGGL((sample_root_kernel<BF16, VEC>), dim3(p.wchunks, p.batch), dim3(kThreads),
                      0, stream, p);
-  hipLaunchKernelGGL((sample_pick_kernel<BF16, VEC>), dim3(p.batch), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((sample_walk_kernel<BF16, VEC>), dim3(p.batch), dim3(kWalkThreads), 0, stream,
                      p);
+  if (p.n_max > 1) {
+    // stops below the root
+    hipLaunchKernelGGL((sample_residual_kernel<BF16, VEC>), dim3(p.wchunks, p.batch),
+                       dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((sample_pick_kernel<BF16, VEC>), dim3(p.batch), dim3(kThreads), 0,
+                       stream, p);
+  }
 }
 
 }  // namespace
@@ -642,6 +1117,22 @@ int32_t sample_stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab) {
 int32_t sample_stat_chunks(graft_dtype dtype, int32_t loads, int32_t vocab) {
   const long long len = (long long)kThreads * loads * (dtype == GRAFT_BF16 ? 8 : 4);
   return (int32_t)((vocab + len - 1) / len);
+}
+
+// Staged mode reads every row of the tree once, wide, so its cost follows
+// the tree's logits and not the walk's depth.  Lazy mode reads the root row
+// wide and each deeper row a walk reaches on one compute unit (about 8 us
+// for 150K entries, arithmetic-bound), so its cost follows the deepest walk
+// of the batch.  Staged while the tree's logits take at most 384 MiB (about
+// 70 us of reading: the deepest walk would have to stop within seven or
+// eight levels for lazy mode to win) and a row's chunk records fit one
+// workgroup's staging area; lazy beyond either.
+constexpr size_t kStagedBytes = size_t{384} << 20;
+
+bool sample_lazy(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab) {
+  const size_t e = dtype == GRAFT_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)batch * n_max * vocab * e;
+  return bytes > kStagedBytes || sample_stat_chunks(dtype, kStatSmall, vocab) > kSampleStage;
 }
 
 int32_t sample_walk_chunks(graft_dtype dtype, int32_t vocab) {

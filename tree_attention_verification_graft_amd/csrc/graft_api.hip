@@ -31,11 +31,15 @@ graft_status check_launch(const char *what) {
 }
 
 SampleLayout sample_layout(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab) {
-  // statistics sized for the smaller chunks (the most per row)
-  const size_t chunks = (size_t)sample_stat_chunks(dtype, 2, vocab);
   const size_t wchunks = (size_t)sample_walk_chunks(dtype, vocab);
+  // staged: the statistics of every row, sized for the smaller chunks (the
+  // most per row); lazy: the root rows' chunk records
+  const size_t recs =
+      sample_lazy(dtype, batch, n_max, vocab)
+          ? (size_t)batch * wchunks * sizeof(RootChunk)
+          : (size_t)batch * n_max * sample_stat_chunks(dtype, 2, vocab) * sizeof(ChunkStat);
   SampleLayout l{};
-  l.off_chunk_w = align_up((size_t)batch * n_max * chunks * sizeof(ChunkStat), 256);
+  l.off_chunk_w = align_up(recs, 256);
   l.off_rec = l.off_chunk_w + align_up((size_t)batch * wchunks * sizeof(double), 256);
   l.total = l.off_rec + align_up((size_t)batch * sizeof(SampleRec), 256);
   return l;
@@ -458,8 +462,6 @@ graft_status graft_accept_sample(graft_dtype dtype, int32_t batch, int32_t n_max
   REQUIRE(k_log2 < 1e37, GRAFT_ERR_UNSUPPORTED, "graft_accept_sample: temperature below 1e-37");
   REQUIRE((long long)batch * n_max <= 65535, GRAFT_ERR_UNSUPPORTED,
           "graft_accept_sample: batch * n_max above 65535");
-  REQUIRE(sample_stat_chunks(dtype, 2, vocab) <= kSampleStage, GRAFT_ERR_UNSUPPORTED,
-          "graft_accept_sample: vocab above %d", kSampleStage * (dtype == GRAFT_BF16 ? 4096 : 2048));
   if (batch == 0) return GRAFT_OK;
   REQUIRE(logits && tree_token && tree_parent && n_nodes && rand_accept && rand_sample &&
               accept_len && path_nodes && path_tokens,
@@ -472,6 +474,7 @@ graft_status graft_accept_sample(graft_dtype dtype, int32_t batch, int32_t n_max
   p.batch = batch;
   p.n_max = n_max;
   p.vocab = vocab;
+  p.lazy = sample_lazy(dtype, batch, n_max, vocab) ? 1 : 0;
   p.stat_loads = sample_stat_loads(dtype, batch * n_max, vocab);
   p.chunks = sample_stat_chunks(dtype, p.stat_loads, vocab);
   p.wchunks = sample_walk_chunks(dtype, vocab);
@@ -489,6 +492,7 @@ graft_status graft_accept_sample(graft_dtype dtype, int32_t batch, int32_t n_max
   p.path_tokens = path_tokens;
   const SampleLayout lay = sample_layout(dtype, batch, n_max, vocab);
   p.stats = static_cast<ChunkStat *>(workspace);
+  p.root = static_cast<RootChunk *>(workspace);
   p.chunk_w = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.off_chunk_w);
   p.rec = reinterpret_cast<SampleRec *>(static_cast<char *>(workspace) + lay.off_rec);
   launch_accept_sample(dtype, p, stream);

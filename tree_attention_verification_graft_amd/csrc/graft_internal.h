@@ -201,9 +201,19 @@ struct alignas(16) SampleRec {
   int32_t gone[GRAFT_MAX_NODES];  // tokens rejected at the stop node
 };
 constexpr int kSampleStage = 2304;  // chunk records one workgroup stages in LDS (36 KB)
+// Statistics of one vocabulary chunk of a root row, relative to the chunk's
+// own max: z sums the float64 masses of all entries, r those of the entries
+// that are not a root child's token (the residual mass when the walk stops
+// at the root).
+struct alignas(16) RootChunk {
+  double z, r;
+  float m;  // chunk max (-inf: no mass)
+  int32_t pad[3];
+};
 struct SampleParams {
   int32_t batch, n_max, vocab;
-  int32_t chunks, stat_loads;  // statistics chunks per row, loads per thread of one
+  int32_t lazy;                // 0: staged mode, 1: lazy mode
+  int32_t chunks, stat_loads;  // staged statistics chunks per row, loads per thread of one
   int32_t wchunks;             // chunks of the stop row's float64 masses
   double k_log2;   // log2(e) / temperature
   float k_hi, k_lo;  // k_log2 split into a float and the float of the rest
@@ -216,18 +226,23 @@ struct SampleParams {
   int32_t *accept_len;
   int32_t *path_nodes;
   int32_t *path_tokens;
-  ChunkStat *stats;  // [batch * n_max][chunks]
+  ChunkStat *stats;  // staged: [batch * n_max][chunks]
+  RootChunk *root;   // lazy: [batch][wchunks] chunk records of the root rows
   double *chunk_w;   // [batch][wchunks] residual mass of the stop row per chunk
   SampleRec *rec;    // [batch]
 };
-// Statistics chunks: loads per thread for a launch over `rows` node rows,
-// and chunks per row at that many loads (2048 or 1024 entries per load).
-int32_t sample_stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab);
-int32_t sample_stat_chunks(graft_dtype dtype, int32_t loads, int32_t vocab);
 // Chunks of the stop row's float64 masses (4096 bf16 or 2048 f32 entries).
 int32_t sample_walk_chunks(graft_dtype dtype, int32_t vocab);
+// Staged statistics chunks: loads per thread for a launch over `rows` node
+// rows, and chunks per row at that many loads (2048 or 1024 entries per
+// load).
+int32_t sample_stat_loads(graft_dtype dtype, int32_t rows, int32_t vocab);
+int32_t sample_stat_chunks(graft_dtype dtype, int32_t loads, int32_t vocab);
+// Whether a call takes lazy mode (the root's records, deeper rows read by
+// the walk) rather than staged mode (statistics of every row).
+bool sample_lazy(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab);
 struct SampleLayout {
-  size_t off_chunk_w, off_rec, total;
+  size_t off_chunk_w, off_rec, total;  // the records (stats or root) at offset 0
 };
 SampleLayout sample_layout(graft_dtype dtype, int32_t batch, int32_t n_max, int32_t vocab);
 void launch_accept_sample(graft_dtype dtype, const SampleParams &p, hipStream_t stream);
