@@ -71,8 +71,9 @@ def test_step_graph_replays_match_eager(name, over):
 
 
 def test_sampling_acceptance_graph_replays_match_eager():
-    """Sampling acceptance (two launches, no memsets) captured once and
-    replayed: every replay equals the eager call bit for bit."""
+    """Sampling acceptance in staged mode (three launches, no memsets)
+    captured once and replayed: every replay equals the eager call bit for
+    bit."""
     import torch
     from tree_attention_verification_graft_amd.pipeline import DeviceStep, to_device
     w = W.make("qwen3_8b_b16", B=4, Hq=8, Hkv=2, prefix=(300, 900), V=5000)
@@ -100,4 +101,60 @@ def test_sampling_acceptance_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name, a, b in zip(("accept_len", "path_nodes", "path_tokens"), ref,
                               (ds.accept_len, ds.path_nodes, ds.path_tokens)):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
+
+
+def test_lazy_sampling_graph_replays_match_eager():
+    """Sampling acceptance in lazy mode (a vocabulary past the staging
+    area: the root launch, the walk, then the residual and pick launches)
+    captured once and replayed.  The batch mixes stops at the root (a
+    root-only tree, and root children without mass), where the walk draws
+    the bonus token, with deeper stops, which go through the last two
+    launches; every replay equals the eager call bit for bit."""
+    import torch
+    from tree_attention_verification_graft_amd import binding as G
+    from tree_attention_verification_graft_amd.pipeline import to_device
+    B, n_max, V = 4, 6, 2304 * 4096 + 1
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((B, n_max, V), dtype=np.float32)
+    parent = np.array([[-1, 0, 1, 2, 3, 0]] * B, np.int32)  # a chain and a root sibling
+    token = rng.integers(0, V, (B, n_max)).astype(np.int32)
+    n_nodes = np.array([n_max, 1, n_max, 3], np.int32)
+    for b in (0, 2, 3):
+        # the chain's tokens dominate their rows, except in sequence 3,
+        # where the root's children carry no mass
+        for c in range(1, int(n_nodes[b])):
+            if b != 3 and parent[b, c] >= 0 and c != 5:
+                x[b, parent[b, c], token[b, c]] = 60.0
+    logits = W.f32_to_bf16_bits(x)
+    ra, rs = W.sampling_uniforms(17, B, n_max)
+    d = "cuda"
+    lg = to_device(logits, d)
+    args = [to_device(a, d) for a in (token, parent, n_nodes, ra, rs)]
+    i32 = torch.int32
+    acc = torch.full((B,), -9, dtype=i32, device=d)
+    pn = torch.full((B, n_max), -9, dtype=i32, device=d)
+    pt = torch.full((B, n_max + 1), -9, dtype=i32, device=d)
+    ws = torch.empty(G.graft_accept_sample_workspace_size("bf16", B, n_max, V),
+                     dtype=torch.uint8, device=d)
+
+    def call():
+        G.graft_accept_sample(lg, 1.0, *args, acc, pn, pt, ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (acc, pn, pt)]
+    # the chain is accepted to its end in sequences 0 and 2, nothing at the
+    # root of sequences 1 and 3
+    assert ref[0].tolist() == [4, 0, 4, 0], ref[0].tolist()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        for t in (acc, pn, pt):
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("accept_len", "path_nodes", "path_tokens"), ref, (acc, pn, pt)):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
