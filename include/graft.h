@@ -67,7 +67,8 @@ enum {
   GRAFT_MAX_STAGES = 8,        /* pruning checkpoints per config */
   GRAFT_MAX_NODES = 128,       /* n_max = kmax + 1 <= 128 */
   GRAFT_MAX_DRAFT = 256,       /* draft nodes per sequence */
-  GRAFT_MAX_TOP_S = 32         /* successors per row of M */
+  GRAFT_MAX_TOP_S = 32,        /* successors per row of M */
+  GRAFT_MAX_VOCAB = 2147418112 /* 2^31 - 2^16: vocabulary chunks index in int32 */
 };
 
 #define GRAFT_MASK_WORDS(n_max) (((n_max) + 31) / 32)
@@ -305,8 +306,8 @@ graft_status graft_tree_attention_rope(graft_dtype dtype, int32_t batch, int32_t
  *   path_tokens     int32 [batch][n_max + 1]: the path's tokens (root token
  *                   first) followed by the accepted node's argmax (bonus),
  *                   -1 padded; accept_len + 2 valid entries
- * Inputs: logits [batch][n_max][vocab] (dtype); tree arrays as produced by
- * graft_build_tree.
+ * Inputs: logits [batch][n_max][vocab] (dtype), vocab <= GRAFT_MAX_VOCAB
+ * (else GRAFT_ERR_UNSUPPORTED); tree arrays as produced by graft_build_tree.
  * workspace: >= graft_accept_workspace_size(...) bytes, any contents (one
  * packed value/index key per node row and vocabulary chunk; chunks hold
  * 2048 to 16384 entries).
@@ -360,7 +361,7 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max,
  * row once, at a cost independent of how deep the walks go; larger ones
  * read the root row and then only the rows a walk reaches, one workgroup
  * per sequence, at a cost that grows with the deepest walk of the batch.
- * Any vocabulary size is accepted.
+ * vocab <= GRAFT_MAX_VOCAB, else GRAFT_ERR_UNSUPPORTED.
  */
 size_t graft_accept_sample_workspace_size(graft_dtype dtype, int32_t batch, int32_t n_max,
                                           int32_t vocab);

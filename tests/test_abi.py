@@ -101,6 +101,8 @@ def test_accept_and_update_validation():
     assert acc(dt=3) == -1
     assert acc(n=200) == -1
     assert acc(v=0) == -1
+    assert acc(v=2**31 - 2**16 + 1) == -2  # chunk bounds would leave int32
+    assert "vocab above" in G.graft_last_error()
     assert acc(wsb=8) == -3
     assert acc(b=0) == 0
     align = lambda x: -(-x // 256) * 256
@@ -166,6 +168,8 @@ def test_accept_sample_validation():
     assert acc(n=0) == -1
     assert acc(n=129) == -1
     assert acc(v=0) == -1
+    assert acc(v=2**31 - 2**16 + 1) == -2  # chunk bounds would leave int32
+    assert "vocab above" in G.graft_last_error()
     assert acc(t=0.0) == -1
     assert acc(t=-1.0) == -1
     assert acc(t=float("inf")) == -1

@@ -405,6 +405,8 @@ graft_status graft_accept(graft_dtype dtype, int32_t batch, int32_t n_max, int32
   REQUIRE(batch >= 0 && batch <= 65535 && n_max >= 1 && n_max <= GRAFT_MAX_NODES,
           GRAFT_ERR_INVALID_ARG, "graft_accept: batch/n_max out of range");
   REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_accept: vocab < 1");
+  REQUIRE(vocab <= GRAFT_MAX_VOCAB, GRAFT_ERR_UNSUPPORTED, "graft_accept: vocab above %d",
+          (int)GRAFT_MAX_VOCAB);
   REQUIRE((long long)batch * n_max <= 65535, GRAFT_ERR_UNSUPPORTED,
           "graft_accept: batch * n_max above 65535");
   if (batch == 0) return GRAFT_OK;
@@ -456,6 +458,8 @@ graft_status graft_accept_sample(graft_dtype dtype, int32_t batch, int32_t n_max
   REQUIRE(batch >= 0 && batch <= 65535 && n_max >= 1 && n_max <= GRAFT_MAX_NODES,
           GRAFT_ERR_INVALID_ARG, "graft_accept_sample: batch/n_max out of range");
   REQUIRE(vocab >= 1, GRAFT_ERR_INVALID_ARG, "graft_accept_sample: vocab < 1");
+  REQUIRE(vocab <= GRAFT_MAX_VOCAB, GRAFT_ERR_UNSUPPORTED,
+          "graft_accept_sample: vocab above %d", (int)GRAFT_MAX_VOCAB);
   REQUIRE(std::isfinite(temperature) && temperature > 0.f, GRAFT_ERR_INVALID_ARG,
           "graft_accept_sample: temperature must be finite and > 0");
   const double k_log2 = 1.4426950408889634 / (double)temperature;
