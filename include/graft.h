@@ -202,7 +202,12 @@ size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch,
  *                    64-key tile each
  *   longest_first    1: ragged batch, (sequence, split) work started longest
  *                    first
- *   workgroups       workgroups of the attention launch
+ *   workgroups       workgroups of the attention launch.  A matrix-core
+ *                    launch has one work item per (sequence, KV head, row
+ *                    group, split), rounded up to a multiple of 8; without
+ *                    longest_first it has at most 256 workgroups (one per
+ *                    compute unit), each running its items back to back,
+ *                    with longest_first one workgroup per item
  */
 typedef struct {
   int32_t matrix_cores, n_row_groups, rows_per_group, n_splits, tiles_per_split,

@@ -256,7 +256,13 @@ def test_attention_plan_query():
         covered = [t for s in range(pl["n_splits"])
                    for t in range(max(0, s * tps - shift), min(tiles, (s + 1) * tps - shift))]
         assert covered == list(range(tiles)), name
-        assert pl["workgroups"] >= B * hkv * pl["n_splits"] * pl["n_row_groups"], name
+        if pl["matrix_cores"]:
+            # one item per (sequence, head, row group, split), a multiple of 8,
+            # run by at most one workgroup per compute unit
+            items = 8 * pl["n_row_groups"] * -(-(B * hkv * pl["n_splits"]) // 8)
+            assert pl["workgroups"] == (items if pl["longest_first"] else min(items, 256)), name
+        else:
+            assert pl["workgroups"] >= B * hkv * pl["n_splits"] * pl["n_row_groups"], name
     assert lib.graft_tree_attention_plan(bf, 1, 17, 8, 2, 128, 100, 0, None) == -1
     assert lib.graft_tree_attention_plan(bf, 1, 17, 8, 3, 128, 100, 0,
                                          ctypes.byref(G.AttentionPlan())) == -1

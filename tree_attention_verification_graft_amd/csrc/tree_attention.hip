@@ -868,17 +868,21 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   }
 }
 
+// One work item of the matrix-core kernel: the (sequence, KV head, row
+// group, prefix split) that item `id` decodes to.  Items are laid out for
+// the XCDs: id = xcd + 8 * slot, and the row groups of one KV stream
+// (sequence, head, split) take consecutive slots on one XCD and share its
+// L2.
 template <int NB, bool ROPE, bool LPT, bool NT>
-__global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
-  __shared__ int32_t s_tpos[ROPE ? GRAFT_MAX_NODES : 1];  // tree positions (rotary path)
-
-  // XCD-aware decode: workgroups are dispatched to the 8 XCDs round-robin,
-  // so id = xcd + 8 * slot.  The row groups of one KV stream (sequence,
-  // head, split) take consecutive slots on one XCD and share its L2.
+__device__ __forceinline__ void attn_mfma_item(const AttnParams &p, int id, uint8_t *smem,
+                                               int32_t *s_tpos) {
+  // the thread index, through an opaque copy: every value derived from it
+  // is computed in the item that uses it, not hoisted out of the item loop
+  // to stay live (and spill) through every item
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   MfmaCtx c;
   {
-    const int id = blockIdx.x;
     const int xcd = id & 7, slot = id >> 3;
     c.rg = slot % p.n_row_groups;
     const int cluster = (slot / p.n_row_groups) * 8 + xcd;
@@ -891,7 +895,7 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
       // dispatcher starts the longest work first whatever the prefix lengths.
       __shared__ int32_t s_w[kMfmaThreads];
       __shared__ int32_t s_pair;
-      const int t = threadIdx.x, S = p.n_splits;
+      const int t = tid, S = p.n_splits;
       const int n_pairs = p.batch * S;  // <= kMfmaThreads (host check)
       int w = -1;
       if (t < n_pairs) {
@@ -924,7 +928,7 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
       c.b = cluster / (p.n_splits * p.hkv);
     }
   }
-  c.tid = threadIdx.x;
+  c.tid = tid;
   c.lane = c.tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
   const bool pair = NB == 1 && p.key_pairs;
@@ -992,6 +996,41 @@ __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
     mfma_wave_body<0, ROPE, true, NT>(p, c, smem, s_tpos);
   } else {
     mfma_wave_body<0, ROPE, false, NT>(p, c, smem, s_tpos);
+  }
+}
+
+// Persistent over the items.  With more items than compute units a
+// uniform plan's grid holds one workgroup per compute unit (the LDS ring
+// fills a unit) and each runs its items back to back, so no workgroup
+// waits on the dispatcher between them: measured per-workgroup timestamps
+// showed each XCD starting its second round of workgroups only once its
+// whole first round had ended.  (Ragged plans launch one workgroup per
+// item: there the dispatcher's longest-first order packs better.)  Workgroup s of an XCD (of W there) takes item slot s in
+// round 0, W - 1 - s in round 1, and so on alternately: the four row
+// groups of a stream move together (their L2 sharing holds) and a
+// workgroup that had a long item next takes a short one (longest-first
+// ranks, and the 17-block row groups).
+template <int NB, bool ROPE, bool LPT, bool NT>
+__global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  __shared__ int32_t s_tpos[ROPE ? GRAFT_MAX_NODES : 1];  // tree positions (rotary path)
+  const int xcd = blockIdx.x & 7;
+  const int per_xcd = gridDim.x >> 3;  // workgroups per XCD (the grid is a multiple of 8)
+  const int s_local = blockIdx.x >> 3;
+  const long clusters = (long)p.batch * p.hkv * p.n_splits;
+  const int n_slots = (int)(p.n_row_groups * ((clusters + 7) / 8));  // item slots per XCD
+  for (int r = 0;; ++r) {
+    const int slot = r * per_xcd + ((r & 1) ? per_xcd - 1 - s_local : s_local);
+    if (slot >= n_slots) break;
+    if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
+    // The item reads the arguments at their uses.  Taken through a pointer
+    // the compiler cannot see to be the same each round, they are loaded
+    // in the round that uses them; otherwise they are hoisted out of the
+    // loop, overflow the scalar registers and spill.
+    typedef const __attribute__((address_space(4))) AttnParams const_params;
+    const_params *kp = (const_params *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    attn_mfma_item<NB, ROPE, LPT, NT>(*(const AttnParams *)kp, xcd + 8 * slot, smem, s_tpos);
   }
 }
 
@@ -1492,14 +1531,18 @@ void launch_mfma(const AttnParams &p, dim3 grid, hipStream_t stream) {
 long attention_workgroups(const AttnPlan &pl, int32_t batch, int32_t hkv) {
   if (pl.mfma) {
     const long clusters = (long)batch * hkv * pl.n_splits;
-    return 8L * pl.n_row_groups * ((clusters + 7) / 8);
+    const long items = 8L * pl.n_row_groups * ((clusters + 7) / 8);
+    return pl.lpt ? items : std::min<long>(items, kComputeUnits);
   }
   return (long)pl.n_splits * hkv * (pl.rows_per_group / 4) * batch;
 }
 
 void launch_attention_bf16_mfma(const AttnParams &p, hipStream_t stream) {
   const long clusters = (long)p.batch * p.hkv * p.n_splits;
-  dim3 grid((unsigned)(8 * p.n_row_groups * ((clusters + 7) / 8)));
+  const long items = 8L * p.n_row_groups * ((clusters + 7) / 8);
+  // ragged batches keep one workgroup per item: the dispatcher's longest-
+  // first order packs their unequal items better than a fixed assignment
+  dim3 grid((unsigned)(p.lpt ? items : std::min<long>(items, kComputeUnits)));
   const int nb = (p.rows_per_group / 16 + kMfmaWaves - 1) / kMfmaWaves;
   switch (nb) {
     case 1: launch_mfma<1>(p, grid, stream); break;
