@@ -173,6 +173,12 @@ EDGE = [
     # GQA group 16 with several row groups and a split prefix
     ("group16_long", "qwen3_235b_share", dict(B=2, Hq=32, Hkv=2, prefix_list=[2500, 4100],
                                               V=3000)),
+    # a uniform plan with more work items than compute units and a partial
+    # last round: 3 row groups x 7 splits over 12 KV streams pad to 264 items
+    # on 256 persistent workgroups, 8 of which run a second item
+    ("persistent_partial_round", "qwen3_8b_b16", dict(B=3, Hq=16, Hkv=4, kmax=32,
+                                                      stage_k_ret=[16, 8, 0], n_draft=32,
+                                                      prefix=(2048, 2048), V=2048)),
 ]
 
 

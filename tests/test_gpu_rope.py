@@ -41,6 +41,10 @@ EDGE = {
     "f32_d128": ("tiny_f32", dict(D=128, V=999, prefix=(77, 77))),
     "group16_long": ("qwen3_235b_share", dict(B=2, Hq=32, Hkv=2, prefix_list=[2500, 4100],
                                               V=3000)),
+    # 264 work items on 256 persistent workgroups (a partial last round)
+    "persistent_partial_round": ("qwen3_8b_b16", dict(B=3, Hq=16, Hkv=4, kmax=32,
+                                                      stage_k_ret=[16, 8, 0], n_draft=32,
+                                                      prefix=(2048, 2048), V=2048)),
 }
 
 
