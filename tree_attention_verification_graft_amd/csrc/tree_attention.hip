@@ -1003,10 +1003,11 @@ __device__ __forceinline__ void attn_mfma_item(const AttnParams &p, int id, uint
 // uniform plan's grid holds one workgroup per compute unit (the LDS ring
 // fills a unit) and each runs its items back to back, so no workgroup
 // waits on the dispatcher between them: measured per-workgroup timestamps
-// showed each XCD starting its second round of workgroups only once its
-// whole first round had ended.  (Ragged plans launch one workgroup per
-// item: there the dispatcher's longest-first order packs better.)  Workgroup s of an XCD (of W there) takes item slot s in
-// round 0, W - 1 - s in round 1, and so on alternately: the four row
+// showed each XCD starting its second wave of workgroups only once its
+// whole first wave had ended.  (Ragged plans launch one workgroup per
+// item: there the dispatcher's longest-first order packs better.)
+// Workgroup s of an XCD (of W there) takes item slot s first, then slot
+// 2W - 1 - s, then 2W + s, and so on, alternating direction: the four row
 // groups of a stream move together (their L2 sharing holds) and a
 // workgroup that had a long item next takes a short one (longest-first
 // ranks, and the 17-block row groups).
