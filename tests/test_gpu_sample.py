@@ -224,6 +224,45 @@ def test_random_trees(dtype, B, n_max, V, T):
          f"{'lazy' if lazy else 'staged'}: ok, ambiguous {amb}")
 
 
+# -inf logits (a masked vocabulary), staged and lazy
+MASKED = [("bf16", 12, 33, 20000, 1.0), ("f32", 12, 17, 9001, 0.3),
+          ("bf16", 24, 65, 140001, 1.0)]
+
+
+@pytest.mark.parametrize("dtype,B,n_max,V,T", MASKED,
+                         ids=[f"{d}-B{b}-n{n}-V{v}" for d, b, n, v, t in MASKED])
+def test_masked_vocabulary(dtype, B, n_max, V, T):
+    """Rows with -inf logits: 30% of the entries at random and a contiguous
+    third of the row, so whole vocabulary chunks carry no mass, and some
+    children proposing a masked token.  A masked token has probability 0:
+    it is never accepted and never drawn as the bonus token."""
+    x, token, parent, n_nodes = _random_case(4100 + V, B, n_max, V, "f32", boost=6.0)
+    rng = np.random.default_rng(4200 + V)
+    x[rng.random(x.shape) < 0.3] = -np.inf
+    for b in range(B):
+        for i in range(n_max):
+            a = int(rng.integers(0, V - V // 3))
+            x[b, i, a:a + V // 3] = -np.inf
+            x[b, i, int(rng.integers(0, V))] = 1.0  # at least one finite entry
+        for i in range(1, int(n_nodes[b])):
+            if rng.random() < 0.2:
+                x[b, parent[b, i], token[b, i]] = -np.inf
+    logits = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    ra, rs = W.sampling_uniforms(31, B, n_max)
+    got = run_sample(logits, dtype, T, token, parent, n_nodes, ra, rs)
+    ref = oracle_sample(logits, dtype, T, token, parent, n_nodes, ra, rs)
+    compare(ref, got, parent, token, n_nodes, V)
+    acc_len, path_nodes, path_tokens = got
+    for b in range(B):
+        L = int(acc_len[b])
+        for j in range(1, L + 1):  # every accepted token had mass in its parent's row
+            assert np.isfinite(x[b, path_nodes[b, j - 1], path_tokens[b, j]]), b
+        assert np.isfinite(x[b, path_nodes[b, L], path_tokens[b, L + 1]]), b  # the bonus too
+    _say(f"[sample] masked {dtype} B={B} n_max={n_max} V={V}: ok, "
+         f"{'lazy' if _lazy(dtype, B, n_max, V) else 'staged'}, "
+         f"accept_len {acc_len.tolist()[:8]}")
+
+
 # staged, and lazy by a vocabulary of more than 2304 chunks (then the root
 # kernel's residual sums leave the rejected tokens out)
 RESIDUAL = [("bf16", 8, 12, 30000), ("f32", 8, 12, 30000),
