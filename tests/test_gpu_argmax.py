@@ -65,14 +65,11 @@ def _rows(n_rows, V, seed):
     return out
 
 
-@pytest.mark.parametrize("B,n_max,V", [(2, 5, 32768), (4, 65, 128256), (3, 7, 1000),
-                                       (3, 7, 999)],
-                         ids=["small_grid", "large_grid", "vocab_1000", "vocab_999_scalar"])
-def test_argmax_crafted_rows(B, n_max, V):
+def _chain_accept(logits_h, dtype):
+    """graft_accept on one chain per sequence (node i's parent is i - 1), and
+    the oracle's greedy verification of the same rows."""
     dev = torch.device("cuda:0")
-    rows = _rows(B * n_max, V, seed=B * 1000 + V)
-    logits_h = rows.reshape(B, n_max, V)
-    # a chain per sequence: node i's parent is i - 1
+    B, n_max, V = logits_h.shape
     n_nodes = np.full(B, n_max, np.int32)
     parent = np.tile(np.arange(-1, n_max - 1, dtype=np.int32), (B, 1))
     token = np.zeros((B, n_max), np.int32)
@@ -81,11 +78,14 @@ def test_argmax_crafted_rows(B, n_max, V):
     for i in range(n_max):
         for j in range(i + 1):
             mask[:, i, j // 32] |= np.uint32(1 << (j % 32))
-    ref = O.accept(logits_h, "bf16", token, parent, n_nodes)
+    ref = O.accept(logits_h, dtype, token, parent, n_nodes)
 
     i32 = torch.int32
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    logits = t(logits_h.view(np.int16)).view(torch.bfloat16)
+    if dtype == "bf16":
+        logits = t(logits_h.view(np.int16)).view(torch.bfloat16)
+    else:
+        logits = t(logits_h.astype(np.float32))
     argmax = torch.empty((B, n_max), dtype=i32, device=dev)
     accept_len = torch.empty(B, dtype=i32, device=dev)
     path_nodes = torch.empty((B, n_max), dtype=i32, device=dev)
@@ -96,4 +96,74 @@ def test_argmax_crafted_rows(B, n_max, V):
                    accept_len, path_nodes, path_tokens, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(argmax.cpu().numpy(), ref["argmax"])
+    np.testing.assert_array_equal(accept_len.cpu().numpy(), ref["accept_len"])
     np.testing.assert_array_equal(path_tokens.cpu().numpy(), ref["path_tokens"])
+    return ref
+
+
+@pytest.mark.parametrize("B,n_max,V", [(2, 5, 32768), (4, 65, 128256), (3, 7, 1000),
+                                       (3, 7, 999)],
+                         ids=["small_grid", "large_grid", "vocab_1000", "vocab_999_scalar"])
+def test_argmax_crafted_rows(B, n_max, V):
+    rows = _rows(B * n_max, V, seed=B * 1000 + V)
+    _chain_accept(rows.reshape(B, n_max, V), "bf16")
+
+
+def _masked_rows(n_rows, V, seed):
+    """Rows of a masked vocabulary (-inf logits), as float32 values, one case
+    per row, cycling over the cases."""
+    rng = np.random.default_rng(seed)
+    ninf, pinf = np.float32(-np.inf), np.float32(np.inf)
+    lowest = np.float32(-3.3895314e38)  # the most negative finite bf16, also finite in f32
+    out = np.empty((n_rows, V), np.float32)
+    for r in range(n_rows):
+        case = r % 6
+        x = rng.standard_normal(V).astype(np.float32)
+        if case == 0:  # a few finite entries among -inf: the largest finite one
+            row = np.full(V, ninf)
+            keep = rng.choice(V, max(V // 100, 2), replace=False)
+            row[keep] = x[keep]
+        elif case == 1:  # every entry -inf: all equal, entry 0
+            row = np.full(V, ninf)
+        elif case == 2:  # -inf everywhere but the lowest finite value once
+            row = np.full(V, ninf)
+            row[int(rng.integers(V))] = lowest
+        elif case == 3:  # -inf everywhere but the last entry
+            row = np.full(V, ninf)
+            row[V - 1] = np.float32(-7.0)
+        elif case == 4:  # half masked, entry 0 masked, one maximum on both sides of
+            # each chunk edge (4096- and 6144-entry chunks): the lower index wins
+            row = x.copy()
+            row[rng.random(V) < 0.5] = ninf
+            row[0] = ninf
+            for edge in (6144, 4096):
+                if edge < V:
+                    row[edge - 1] = row[edge] = np.float32(12.0)
+        else:  # +inf twice among -inf and finite entries: the first +inf
+            row = x.copy()
+            row[rng.random(V) < 0.5] = ninf
+            a, b = sorted(rng.choice(V, 2, replace=False).tolist())
+            row[a] = row[b] = pinf
+        out[r] = row
+    return out
+
+
+@pytest.mark.parametrize("dtype,B,n_max,V", [("bf16", 2, 6, 32768), ("bf16", 4, 65, 128256),
+                                             ("bf16", 3, 7, 999), ("f32", 2, 6, 32768),
+                                             ("f32", 3, 7, 999), ("f32", 2, 33, 151936)],
+                         ids=["bf16_small_grid", "bf16_large_grid", "bf16_vocab_999",
+                              "f32_small_grid", "f32_vocab_999", "f32_large"])
+def test_argmax_masked_vocabulary(dtype, B, n_max, V):
+    """-inf logits (a masked vocabulary) order below every finite value and tie
+    with each other; a row of -inf only takes entry 0, and +inf orders above
+    every finite value."""
+    rows = _masked_rows(B * n_max, V, seed=B * 77 + V).reshape(B, n_max, V)
+    logits_h = W.f32_to_bf16_bits(rows) if dtype == "bf16" else rows
+    ref = _chain_accept(logits_h, dtype)
+    # the oracle's argmax itself on the crafted cases it decides
+    am = ref["argmax"].reshape(-1)
+    for r in range(B * n_max):
+        if r % 6 == 1:
+            assert am[r] == 0
+        elif r % 6 == 3:
+            assert am[r] == V - 1
