@@ -26,7 +26,7 @@ def dma_hazards(asm_text):
     lines = asm_text.splitlines()
     total, bad = 0, []
     for i, line in enumerate(lines):
-        m = re.search(r"global_load_lds_dwordx4 v\d+, s\[(\d+):(\d+)\]", line)
+        m = re.search(r"global_load_lds_dword(?:x[34])? v\d+, s\[(\d+):(\d+)\]", line)
         if not m:
             continue
         total += 1
@@ -58,6 +58,9 @@ def test_detector_flags_a_short_distance():
     safe = ("v_readfirstlane_b32 s26, v2\n;;#ASMSTART\ns_nop 4\n"
             "global_load_lds_dwordx4 v48, s[26:27]\n")
     assert dma_hazards(unsafe)[1] and not dma_hazards(safe)[1]
+    # the 4-byte form (the ancestor masks) is checked the same way
+    assert dma_hazards(unsafe.replace("dwordx4", "dword"))[1]
+    assert dma_hazards(safe.replace("dwordx4", "dword")) == (1, [])
 
 
 def test_attention_lds_dma_loads_have_their_wait_states(tmp_path):

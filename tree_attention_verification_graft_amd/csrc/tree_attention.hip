@@ -190,12 +190,20 @@ __device__ inline void load_mask4(uint32_t (&mw)[4], const uint32_t *src, int wo
 // groups.  Each wave
 // issues exactly kDmaPerStage loads per stage (a page past the prefix is
 // redirected to the tile's first page and later masked), so vmcnt counts
-// stay exact.
+// stay exact.  Without rotary embedding the tree tiles follow the prefix
+// tiles through the same ring: K rows as for the prefix, V rows key-major,
+// transposed in LDS when the tile comes up (node ids past the tree are
+// clamped to the last node, whose keys get masked and values zeroed).
 constexpr int kStages = 4;
 constexpr int kKBytes = kTile * kD * 2;  // 16 KB
 constexpr int kVBytes = kD * kTile * 2;  // 16 KB
 constexpr int kStageBytes = kKBytes + kVBytes;
-constexpr int kDmaPerStage = 4;          // per wave: 2 K + 2 V instructions
+constexpr int kDmaPerStage = 4;          // per wave: four 1 KB blocks of one page (K or V)
+// Behind the ring: a sequence's ancestor masks (n_max * words <= 128 * 4
+// words), one 64-word block per wave.
+constexpr int kMaskBytes = kMfmaWaves * 64 * 4;
+static_assert(GRAFT_MAX_NODES * ((GRAFT_MAX_NODES + 31) / 32) <= kMfmaWaves * 64,
+              "a sequence's ancestor masks fill at most one dword per lane");
 
 // Issue one asynchronous 16-byte-per-lane global->LDS load from
 // base + voffset (base wave-uniform, in SGPRs).  lds_base is the
@@ -217,6 +225,13 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voffset, uint32
 }
 __device__ __forceinline__ void dma16_nt(const void *base, uint32_t voffset, uint32_t lds_base) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voffset), "s"(base), "{m0}"(lds_base)
+               : "memory");
+}
+// The 4-byte form (lane bytes at M0 + 4 * lane), for the ancestor masks.
+__device__ __forceinline__ void dma4(const void *base, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1"
                :
                : "v"(voffset), "s"(base), "{m0}"(lds_base)
                : "memory");
@@ -531,7 +546,8 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
   // cores busy through much of its own softmax.  Three blocks do not leave
   // the registers for two halves of scores, so there the halves run one
   // after the other.
-  auto compute = [&](int st, int key0, bool tree) {
+  // (K from stage st, V from stage vst)
+  auto compute = [&](int st, int key0, bool tree, int vst) {
     if constexpr (PAIR) {
       f32x4 sc[NQ][2];
       float mx[NQ];
@@ -539,7 +555,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       qk_half(st, c.khalf, sc);
       rescale_half(mx, prep_half(c.khalf, key0, tree, sc, mx));
       exp_half(sc, pb);
-      pv_half(st, c.khalf, pb);
+      pv_half(vst, c.khalf, pb);
     } else if constexpr (NA <= 2) {
       f32x4 sa[NQ][2], sb[NQ][2];
       float ma[NQ], mb[NQ];
@@ -548,11 +564,11 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       rescale_half(ma, prep_half(0, key0, tree, sa, ma));
       exp_half(sa, pa);
       qk_half(st, 1, sb);
-      pv_half(st, 0, pa);
+      pv_half(vst, 0, pa);
       const uint32_t rb = prep_half(1, key0, tree, sb, mb);
       rescale_half(mb, rb);
       exp_half(sb, pz);
-      pv_half(st, 1, pz);
+      pv_half(vst, 1, pz);
     } else {
 #pragma unroll 1
       for (int kp = 0; kp < 2; ++kp) {
@@ -562,72 +578,86 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
         qk_half(st, kp, sc);
         rescale_half(mx, prep_half(kp, key0, tree, sc, mx));
         exp_half(sc, pb);
-        pv_half(st, kp, pb);
+        pv_half(vst, kp, pb);
       }
     }
   };
 
-  // ---- prefix tiles through the stage ring.  Prologue: the first two
-  // stages are issued behind the query loads and the wait for both is made
-  // visible to the compiler (otherwise it would drain every load in flight
-  // before the first matrix op of each tile); later stages are issued one
-  // tile ahead of use with page ids fetched by scalar loads a tile earlier.
-  // ---- prefix tiles through the stage ring.  Prologue: the first two
-  // stages are issued behind the query loads and the wait for both is made
-  // visible to the compiler (otherwise it would drain every load in flight
-  // before the first matrix op of each tile); later stages are issued three
-  // tiles ahead of use with page ids fetched by scalar loads a tile earlier.
-  int page_next = 0;
-  if (c.n_pref > 0) issue_prefix(0, fix_page(c.pre_page[0], 0));
-  if (c.n_pref > 1) issue_prefix(1, fix_page(c.pre_page[1], 1));
-  if (c.n_pref > 2) page_next = fix_page(c.pre_page[2], 2);
-  // Waves with at most one block have the registers to hold the first tree
-  // tile (keys 0..63) and their ancestor masks from here on, so its loads
-  // go out with the queries instead of one global round trip before the
-  // tree tile (the workgroups of split 0 end last by that much otherwise).
-  constexpr bool kTreePre = NA <= 1 && !ROPE;
+  // ---- the tiles through the stage ring: the prefix tiles, then (without
+  // rotary embedding) the tree tiles.  Prologue: the first two stages are
+  // issued behind the query loads and the wait for both is made visible to
+  // the compiler (otherwise it would drain every load in flight before the
+  // first matrix op of each tile); later stages are issued three tiles
+  // ahead of use, prefix page ids fetched by scalar loads a tile earlier.
+  constexpr bool kTreeRing = !ROPE;
+  const int n_ring = c.n_pref + (kTreeRing ? c.n_tree : 0);
   const __bf16 *k_tree = static_cast<const __bf16 *>(p.k_tree);
   const __bf16 *v_tree = static_cast<const __bf16 *>(p.v_tree);
-  uint4 tk[kTreePre ? 2 : 1], tv[kTreePre ? 8 : 1];
-  // (branch-free: rows past the tree read node n_nodes - 1 and are then
-  // zeroed, and the V part is taken by whole waves 0 and 1, so that the
-  // loads open no divergent region ahead of the DMA ring)
-  auto load_tree = [&](int key0, uint4 (&k2)[2], uint4 (&v8)[8]) {
+  // Tree tile tt: each wave loads the 16 nodes tt * 64 + 16 * my_page ..
+  // + 15 (ids clamped to the last node), waves 0..3 their K rows into the
+  // swizzled rows of the K tile (chunk and row from the prefix offsets),
+  // waves 4..7 their V rows key-major (key at 256 bytes * key) into the V
+  // tile, to be transposed when the tile comes up.
+  auto issue_tree = [&](int st, int tt) {
+    // the arguments through an opaque copy of their address, so that they
+    // are loaded here, where a prefix iteration issues a tree tile, instead
+    // of being hoisted to stay live (and spill) through the prefix loop
+    typedef const __attribute__((address_space(4))) AttnParams const_params;
+    const_params *ka = (const_params *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
     const int last = max(c.n_nodes - 1, 0);
+    const int key_base = tt * kTile + 16 * my_page;
+    const uint32_t node_stride = (uint32_t)ka->hkv * (kD * 2);
+    const uint64_t ba = (uint64_t)(uintptr_t)(
+        reinterpret_cast<const char *>(my_v ? ka->v_tree : ka->k_tree) +
+        ((size_t)c.b * ka->n_max * ka->hkv + c.h) * (kD * 2));
+    const uint32_t ba_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ba >> 32));
+    const uint32_t ba_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ba);
+    const char *base =
+        reinterpret_cast<const char *>(((uint64_t)ba_hi << 32) | (uint64_t)ba_lo);
+    const uint32_t sbase = c.lds0 + st * kStageBytes;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int ch = tid + kMfmaThreads * r;
-      const int j = key0 + (ch >> 4);
-      const uint4 x = *reinterpret_cast<const uint4 *>(
-          k_tree + (((size_t)c.b * p.n_max + min(j, last)) * p.hkv + c.h) * kD + (ch & 15) * 8);
-      k2[r] = j < c.n_nodes ? x : zero4();
-    }
-    if (wave < 2) {  // tid < 128
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = key0 + 8 * (tid >> 4) + i;
-        const uint4 x = *reinterpret_cast<const uint4 *>(
-            v_tree + (((size_t)c.b * p.n_max + min(j, last)) * p.hkv + c.h) * kD +
-            (tid & 15) * 8);
-        v8[i] = j < c.n_nodes ? x : zero4();
-      }
+    for (int q = 0; q < 4; ++q) {
+      // K: dma_off holds (key within the page) * 256 + the swizzled chunk's
+      // offset; V: key 4 q + lane / 16 of the wave's 16, chunk lane % 16
+      const int kq = my_v ? 4 * q + (lane >> 4) : (int)(dma_off[q] >> 8);
+      const uint32_t chunk = my_v ? (uint32_t)(lane & 15) << 4 : (dma_off[q] & 255u);
+      const uint32_t off = (uint32_t)min(key_base + kq, last) * node_stride + chunk;
+      dma16(base, off, sbase + dma_dst(q));
     }
   };
+  auto issue_tile = [&](int v, int page) {
+    if (kTreeRing && v >= c.n_pref) issue_tree(v % kStages, v - c.n_pref);
+    else issue_prefix(v % kStages, page);
+  };
+  int page_next = 0;
+  if (n_ring > 0) issue_tile(0, fix_page(c.pre_page[0], 0));
+  if (n_ring > 1) issue_tile(1, fix_page(c.pre_page[1], 1));
+  if (c.n_pref > 2) page_next = fix_page(c.pre_page[2], 2);
+  // The sequence's ancestor masks go to LDS with the queries: wave w copies
+  // words 64 w .. + 63 of its mask rows (indices clamped to the rows), one
+  // dword per lane, landed by the wait below.
+  uint32_t *s_mask = reinterpret_cast<uint32_t *>(smem + kStages * kStageBytes);
+  if (c.n_tree > 0) {
+    const uint32_t n_words = (uint32_t)(p.n_max * p.words);  // <= 512 (host check)
+    const uint64_t ma =
+        (uint64_t)(uintptr_t)(p.tree_mask + (size_t)c.b * p.n_max * p.words);
+    const uint32_t ma_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ma >> 32));
+    const uint32_t ma_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ma);
+    const char *mbase =
+        reinterpret_cast<const char *>(((uint64_t)ma_hi << 32) | (uint64_t)ma_lo);
+    const uint32_t widx = min((uint32_t)(64 * wave + lane), n_words - 1u);
+    dma4(mbase, widx * 4u, c.lds0 + kStages * kStageBytes + 256u * wave);
+  }
   auto load_masks = [&]() {
 #pragma unroll
     for (int k = 0; k < NA; ++k) {
       const int r = row_of(k);
       const int node = r < c.rows_b ? r / c.G : 0;
-      load_mask4(tmask[k], p.tree_mask + ((size_t)c.b * p.n_max + node) * p.words, p.words);
+      load_mask4(tmask[k], s_mask + node * p.words, p.words);
     }
   };
-  if constexpr (kTreePre) {
-    if (c.n_tree > 0) {
-      load_masks();
-      load_tree(0, tk, tv);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries and stages 0, 1
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries, masks and stages 0, 1
   if (ROPE) {
     // the lane holds dims 32 kk + 8 g4 + j; kk and kk + 2 are the pairs
     // (i, i + 64), rotated in fp32 and rounded once to bf16
@@ -654,19 +684,17 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
     // barrier)
     if (tid < p.n_max) s_tpos[tid] = c.tpos;
   }
-  if (c.n_pref > 2) issue_prefix(2, page_next);
+  if (n_ring > 2) issue_tile(2, page_next);
   if (c.n_pref > 3) page_next = tile_page(3);
-  for (int it = 0; it < c.n_pref; ++it) {
-    // stage `it` has landed once at most the loads issued after it remain
-    const int after = min(c.n_pref - 1 - it, kStages - 2);
+  // stage `it` has landed once at most the loads issued after it remain
+  auto wait_stage = [&](int it) {
+    const int after = min(n_ring - 1 - it, kStages - 2);
     if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
     else if (after == 1) wait_vmcnt<kDmaPerStage>();
     else wait_vmcnt<0>();
     lds_barrier();  // every wave's loads for stage `it` are in LDS; stage it-1 is free
-    if (it + kStages - 1 < c.n_pref) {
-      issue_prefix((it + kStages - 1) % kStages, page_next);
-      if (it + kStages < c.n_pref) page_next = tile_page(it + kStages);
-    }
+  };
+  auto prefix_tile = [&](int it) {
     const int st = it % kStages;
     const int key0 = (c.t_begin + it) * kTile;
     if (key0 + kTile > c.P) {
@@ -680,49 +708,87 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       }
       lds_barrier();
     }
-    if (NA > 0) compute(st, key0, false);
+    if (NA > 0) compute(st, key0, false, st);
+  };
+  // Two loops over the prefix tiles, so that the main one, whose
+  // iterations each issue the prefix tile three ahead, carries no test
+  // for the tree tiles (a taken branch per tile costs more than the code
+  // it would save); the last three prefix tiles issue the tree tiles.
+  const int n_main = max(c.n_pref - (kStages - 1), 0);
+  for (int it = 0; it < n_main; ++it) {
+    wait_vmcnt<2 * kDmaPerStage>();  // two tiles are issued after this one
+    lds_barrier();  // every wave's loads for stage `it` are in LDS; stage it-1 is free
+    issue_prefix((it + kStages - 1) % kStages, page_next);
+    if (it + kStages < c.n_pref) page_next = tile_page(it + kStages);
+    prefix_tile(it);
+  }
+  for (int it = n_main; it < c.n_pref; ++it) {
+    wait_stage(it);
+    if (kTreeRing && it + kStages - 1 < n_ring)
+      issue_tree((it + kStages - 1) % kStages, it + kStages - 1 - c.n_pref);
+    prefix_tile(it);
   }
 
-  // ---- tree tiles (split 0 only): the keys are the tree nodes themselves.
-  if (!kTreePre && c.n_tree > 0) load_masks();
-  for (int tt = 0; tt < c.n_tree; ++tt) {
+  // ---- tree tiles from the ring (split 0 only): the keys are the tree
+  // nodes themselves.  A loop of its own, so that the masks and the
+  // transposition's registers are live here only.
+  if (kTreeRing && c.n_tree > 0) load_masks();
+  // (a tree has at most two tiles, and the ring runs three ahead, so every
+  // tree tile has been issued by the time the first one comes up)
+  static_assert((GRAFT_MAX_NODES + kTile - 1) / kTile <= kStages - 1,
+                "the tree tiles are issued from the prefix loop and the prologue");
+  for (int it = c.n_pref; it < n_ring; ++it) {
+    wait_stage(it);
+    const int st = it % kStages;
+    const int key0 = (it - c.n_pref) * kTile;
+    // V key-major -> dim rows in the V part of stage it + 2, which no tile
+    // uses any more (the ring holds at most the next tree tile): thread
+    // t < 128 reads the 8 x 8 block of keys 8 kc .. + 7 and dims 8 dc .. + 7
+    // (keys past the tree as zeros) and writes it transposed as eight
+    // 16-byte dim rows
+    const int vst = (it + 2) % kStages;
+    if (wave < 2) {
+      const uint8_t *sR = smem + st * kStageBytes + kKBytes;
+      uint8_t *sV = smem + vst * kStageBytes + kKBytes;
+      const int dc = tid & 15, kc = (tid >> 4) & 7;
+      uint32_t w[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kl = 8 * kc + i;
+        const uint4 vv = key0 + kl < c.n_nodes
+                             ? *reinterpret_cast<const uint4 *>(sR + kl * 256 + dc * 16)
+                             : zero4();
+        w[i][0] = vv.x;
+        w[i][1] = vv.y;
+        w[i][2] = vv.z;
+        w[i][3] = vv.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = e >> 1;
+        uint32_t o4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a = w[2 * m][q], b2 = w[2 * m + 1][q];
+          o4[m] = (e & 1) ? ((a >> 16) | (b2 & 0xffff0000u)) : ((a & 0xffffu) | (b2 << 16));
+        }
+        const int d = dc * 8 + e;
+        *reinterpret_cast<uint4 *>(sV + (kc >> 1) * 4096 + d * 32 +
+                                   (((kc & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4)) =
+            make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      }
+    }
+    lds_barrier();
+    if (NA > 0) compute(st, key0, true, vst);
+  }
+
+  // ---- tree tiles with rotary embedding (split 0 only): the keys are
+  // rotated by their tree positions on the way into LDS.
+  if (!kTreeRing && c.n_tree > 0) load_masks();
+  for (int tt = 0; tt < (kTreeRing ? 0 : c.n_tree); ++tt) {
     const int key0 = tt * kTile;
     uint8_t *sK = smem;  // stage 0 (all prefix loads have completed)
     uint8_t *sV = smem + kKBytes;
-    if constexpr (kTreePre) {
-      // K chunks as loaded; V 8 x 8 blocks transposed in registers (below)
-      if (tt > 0) load_tree(key0, tk, tv);
-      wait_vmcnt<0>();
-      lds_barrier();
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int ch = tid + kMfmaThreads * r;
-        const int R = k_row_of_key(ch >> 4);
-        *reinterpret_cast<uint4 *>(sK + R * 256 + (((ch & 15) ^ (R & 15)) << 4)) = tk[r];
-      }
-      if (tid < 128) {
-        const int dc = tid & 15, kc = tid >> 4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int q = e >> 1;
-          uint32_t o4[4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint4 &va = tv[2 * m], &vb = tv[2 * m + 1];
-            const uint32_t a = q == 0 ? va.x : q == 1 ? va.y : q == 2 ? va.z : va.w;
-            const uint32_t b2 = q == 0 ? vb.x : q == 1 ? vb.y : q == 2 ? vb.z : vb.w;
-            o4[m] = (e & 1) ? ((a >> 16) | (b2 & 0xffff0000u)) : ((a & 0xffffu) | (b2 << 16));
-          }
-          const int d = dc * 8 + e;
-          *reinterpret_cast<uint4 *>(sV + (kc >> 1) * 4096 + d * 32 +
-                                     (((kc & 1) ^ (((d >> 2) ^ (d >> 3)) & 1)) << 4)) =
-              make_uint4(o4[0], o4[1], o4[2], o4[3]);
-        }
-      }
-      lds_barrier();
-      if (NA > 0) compute(0, key0, true);
-      continue;
-    }
     wait_vmcnt<0>();
     lds_barrier();
 #pragma unroll
@@ -794,7 +860,7 @@ __device__ __forceinline__ void mfma_wave_body(const AttnParams &p, const MfmaCt
       }
     }
     lds_barrier();
-    if (NA > 0) compute(0, key0, true);
+    if (NA > 0) compute(0, key0, true, 0);
   }
 
   // ---- key pairs: the wave of the second half hands its (O, max, sum)
@@ -1013,7 +1079,7 @@ __device__ __forceinline__ void attn_mfma_item(const AttnParams &p, int id, uint
 // ranks, and the 17-block row groups).
 template <int NB, bool ROPE, bool LPT, bool NT>
 __global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes + kMaskBytes];
   __shared__ int32_t s_tpos[ROPE ? GRAFT_MAX_NODES : 1];  // tree positions (rotary path)
   const int xcd = blockIdx.x & 7;
   const int per_xcd = gridDim.x >> 3;  // workgroups per XCD (the grid is a multiple of 8)
