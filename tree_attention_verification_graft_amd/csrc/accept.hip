@@ -59,21 +59,6 @@ __device__ inline unsigned long long pack(uint32_t ord, int idx) {
 __device__ inline unsigned long long umax64(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
-// Order-preserving int16 keys of the two bf16 values in a word, by packed
-// 16-bit integer ops: a negative value flips its magnitude bits (so larger
-// magnitudes order lower) and moves up by one, which folds -0 onto +0.  A
-// key of -32768 is below every value's (the most negative finite value maps
-// to -32639), so it marks entries outside the chunk.
-typedef short short2v __attribute__((ext_vector_type(2)));
-__device__ inline short2v okey2(uint32_t w) {
-  const short2v x = __builtin_bit_cast(short2v, w);
-  const short2v s = x >> (short2v){15, 15};  // 0 or -1 per half
-  return (x ^ (s & (short2v){0x7fff, 0x7fff})) - s;
-}
-// The bf16 bits of a key (either zero for key 0).
-__device__ inline uint32_t key_bf16(int key) {
-  return key >= 0 ? (uint32_t)key : (uint32_t)(((key - 1) ^ 0x7fff) & 0xffff);
-}
 __device__ inline int wave_max_i32(int v) {
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
   return v;

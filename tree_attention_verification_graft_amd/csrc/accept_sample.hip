@@ -451,16 +451,51 @@ __global__ __launch_bounds__(kThreads) void chunk_stats_kernel(SampleParams p) {
   const int b = row / p.n_max, i = row % p.n_max;
   if (i >= max(p.n_nodes[b], 1)) return;  // rows past the tree are not read
   float v[kV];
-  load_strided<BF16, VEC, L>(p.logits, (size_t)row, p.vocab, c * kThreads * kV, v);
   __shared__ float red[kWaves];
+  __shared__ int ired[kWaves];
   __shared__ double zred[kWaves];
   float m = -INFINITY;
+  if constexpr (BF16 && VEC) {
+    // bf16 words as loaded: the maximum by packed 16-bit order keys (two
+    // values per op, -0 folded onto +0), then the values unpacked for the
+    // exponentials; loads past the vocabulary hold -inf pairs
+    const int lo = c * kThreads * kV, hi = min(p.vocab, lo + kThreads * kV);
+    const u32x4 *x = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.logits) +
+                                                     (size_t)row * p.vocab * 2);
+    u32x4 raw[L];
 #pragma unroll
-  for (int k = 0; k < kV; ++k) m = fmaxf(m, v[k]);
-  m = wave_max_f(m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    for (int k = 0; k < L; ++k) {
+      const int e = lo + (k * kThreads + (int)threadIdx.x) * kPer;
+      raw[k] = e < hi ? __builtin_nontemporal_load(x + e / kPer)
+                      : (u32x4){0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+    }
+    short2v acc = (short2v){-32768, -32768};
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = __builtin_elementwise_max(acc, okey2(raw[k][q]));
+    int km = max((int)acc.x, (int)acc.y);
+    for (int o = 32; o > 0; o >>= 1) km = max(km, __shfl_xor(km, o));
+    if ((threadIdx.x & 63) == 0) ired[threadIdx.x >> 6] = km;
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[k * 8 + 2 * q] = __uint_as_float(raw[k][q] << 16);
+        v[k * 8 + 2 * q + 1] = __uint_as_float(raw[k][q] & 0xffff0000u);
+      }
+    __syncthreads();
+    km = max(max(ired[0], ired[1]), max(ired[2], ired[3]));
+    m = __uint_as_float(key_bf16(km) << 16);
+  } else {
+    load_strided<BF16, VEC, L>(p.logits, (size_t)row, p.vocab, c * kThreads * kV, v);
+#pragma unroll
+    for (int k = 0; k < kV; ++k) m = fmaxf(m, v[k]);
+    m = wave_max_f(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
   // each load's values summed pairwise in float32 (three roundings at
   // most), the loads' sums in float64
   double z = 0.0;
