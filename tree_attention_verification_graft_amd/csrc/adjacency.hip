@@ -663,8 +663,9 @@ UpdateLayout update_layout(uint32_t capacity) {
 void launch_update(const UpdateParams &p, hipStream_t stream) {
   if (p.max_transitions <= kSmallT) {
     // enough workgroups that every touched row (at most one per transition)
-    // gets a wave of its own
-    const int groups = std::max(1, std::min(64, (p.max_transitions + kSmallWaves - 1) / kSmallWaves));
+    // gets a wave of its own (at most 256 at kSmallT transitions; a cap of 64
+    // left two rows per wave at 2,080 transitions, one more round trip)
+    const int groups = std::max(1, (p.max_transitions + kSmallWaves - 1) / kSmallWaves);
     hipLaunchKernelGGL(update_small_kernel, dim3(groups), dim3(kSmallThreads), 0, stream, p);
     return;
   }
