@@ -68,6 +68,7 @@ enum {
   GRAFT_MAX_NODES = 128,       /* n_max = kmax + 1 <= 128 */
   GRAFT_MAX_DRAFT = 256,       /* draft nodes per sequence */
   GRAFT_MAX_TOP_S = 32,        /* successors per row of M */
+  GRAFT_MAX_KV_HEADS = 65536,  /* hkv: per-page and per-node byte offsets fit 32 bits */
   GRAFT_MAX_VOCAB = 2147418112 /* 2^31 - 2^16: vocabulary chunks index in int32 */
 };
 
@@ -173,7 +174,8 @@ graft_status graft_build_tree(const graft_tree_config *cfg, int32_t batch,
  *                    to the workspace query.
  * Arithmetic: fp32 accumulation; bf16 output rounded to nearest even.
  * Supported: block_size 16; head_dim 64 or 128 (bf16 with head_dim 128 takes
- * the matrix-core path when n_nodes * group >= 16 rows).
+ * the matrix-core path when n_nodes * group >= 16 rows); hkv <=
+ * GRAFT_MAX_KV_HEADS, else GRAFT_ERR_UNSUPPORTED.
  * workspace: >= graft_tree_attention_workspace_size(...) bytes, any contents.
  */
 size_t graft_tree_attention_workspace_size(graft_dtype dtype, int32_t batch,

@@ -78,6 +78,9 @@ def test_attention_validation():
     assert _attn(D=96) == -2
     assert _attn(block=32) == -2
     assert _attn(hq=6, hkv=4) == -1
+    # per-node and per-page byte offsets of the KV tensors are 32-bit
+    assert _attn(hq=65537, hkv=65537) == -2
+    assert "hkv 65537 above 65536" in G.graft_last_error()
     assert _attn(n_max=129) == -1
     assert _attn(max_blocks=2) == -1                          # 2*16 < max_prefix
     assert _attn(scale=float("inf")) == -1
@@ -266,6 +269,8 @@ def test_attention_plan_query():
     assert lib.graft_tree_attention_plan(bf, 1, 17, 8, 2, 128, 100, 0, None) == -1
     assert lib.graft_tree_attention_plan(bf, 1, 17, 8, 3, 128, 100, 0,
                                          ctypes.byref(G.AttentionPlan())) == -1
+    assert lib.graft_tree_attention_plan(bf, 1, 17, 65537, 65537, 128, 100, 0,
+                                         ctypes.byref(G.AttentionPlan())) == -2
 
 
 def test_noalloc_rejects_plans_beyond_its_scratch():

@@ -189,6 +189,8 @@ static graft_status check_attn_shape(graft_dtype dtype, int32_t batch, int32_t n
           "graft_tree_attention: batch/n_max out of range");
   REQUIRE(hq >= 1 && hkv >= 1 && hq % hkv == 0, GRAFT_ERR_INVALID_ARG,
           "graft_tree_attention: hq must be a positive multiple of hkv");
+  REQUIRE(hkv <= GRAFT_MAX_KV_HEADS, GRAFT_ERR_UNSUPPORTED,
+          "graft_tree_attention: hkv %d above %d", hkv, (int)GRAFT_MAX_KV_HEADS);
   REQUIRE(head_dim == 64 || head_dim == 128, GRAFT_ERR_UNSUPPORTED,
           "graft_tree_attention: head_dim %d not supported (64 or 128)", head_dim);
   REQUIRE(max_prefix >= 0, GRAFT_ERR_INVALID_ARG, "graft_tree_attention: max_prefix < 0");
