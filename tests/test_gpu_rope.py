@@ -45,6 +45,10 @@ EDGE = {
     "persistent_partial_round": ("qwen3_8b_b16", dict(B=3, Hq=16, Hkv=4, kmax=32,
                                                       stage_k_ret=[16, 8, 0], n_draft=32,
                                                       prefix=(2048, 2048), V=2048)),
+    # one row group of 17 blocks, split 0 with 0, 1 and 2 prefix tiles
+    "three_block_short_prefixes": ("qwen3_8b_b16", dict(B=6, Hq=32, Hkv=8,
+                                                        prefix_list=[3000, 3000, 0, 64, 100,
+                                                                     3000], V=2048)),
 }
 
 
