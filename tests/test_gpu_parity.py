@@ -185,6 +185,10 @@ EDGE = [
     ("three_block_short_prefixes", "qwen3_8b_b16", dict(B=6, Hq=32, Hkv=8,
                                                         prefix_list=[3000, 3000, 0, 64, 100,
                                                                      3000], V=2048)),
+    # the same with two row groups of 9 and 8 blocks (two-block waves)
+    ("two_block_short_prefixes", "qwen3_8b_b16", dict(B=6, Hq=32, Hkv=8,
+                                                      prefix_list=[3000, 0, 64, 100, 2000, 130],
+                                                      V=2048)),
 ]
 
 

@@ -49,6 +49,10 @@ EDGE = {
     "three_block_short_prefixes": ("qwen3_8b_b16", dict(B=6, Hq=32, Hkv=8,
                                                         prefix_list=[3000, 3000, 0, 64, 100,
                                                                      3000], V=2048)),
+    # two row groups of 9 and 8 blocks, split 0 with 0 to 3 prefix tiles
+    "two_block_short_prefixes": ("qwen3_8b_b16", dict(B=6, Hq=32, Hkv=8,
+                                                      prefix_list=[3000, 0, 64, 100, 2000, 130],
+                                                      V=2048)),
 }
 
 
